@@ -1,0 +1,218 @@
+/*
+ * hsma_trsm.h - C ABI of the MI355X (gfx950) triangular-solve library.
+ *
+ * The operation is the left-side, lower-triangular, non-transposed,
+ * non-unit-diagonal TRSM on a square matrix (HSMA-TRSM news summary, first
+ * paragraph: "the left-side lower-triangular case, run with square matrices"):
+ *
+ *     solve  A * X = alpha * B   for X,  X overwrites B,
+ *
+ * where only the lower triangle of A, diagonal included, is read; the stored
+ * upper triangle may hold anything (NaN included) and is never read.
+ * Two regimes follow the HSMA-TRSM paper: m <= 64 is solved directly on chip
+ * (the paper's small-scale section), larger m by blocked TRSM whose diagonal
+ * blocks are inverted in parallel and applied with matrix-multiply updates
+ * (the paper's blocked section and its adaptive block size).
+ *
+ * Conventions for every entry point:
+ *   - Storage is column-major unless stated: element (i, j) of A is at
+ *     A[i + j*lda]. Sizes and strides are counted in elements (a complex
+ *     number is one element), never in bytes.
+ *   - Pointers are device pointers (HBM). The caller owns all of A, B and X;
+ *     the library never keeps them after the call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream). They return once the work is enqueued. A kernel fault surfaces
+ *     at the caller's next synchronisation.
+ *   - Workspace for the blocked path is allocated stream-ordered on `stream`
+ *     (hipMallocAsync / hipFreeAsync), so calls on different streams do not
+ *     share memory.
+ *   - No singularity check: a zero or NaN diagonal entry produces inf/NaN
+ *     under IEEE rules (the SOLVE_TRI review in llama.cpp PR #17457 dropped
+ *     its zero-pivot guard for the same reason).
+ *   - m == 0, n == 0 or batch_count == 0: success, no memory touched.
+ *     alpha == 0: B is set to zero and A is not read.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef HSMA_TRSM_H
+#define HSMA_TRSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int hsma_status;
+#define HSMA_STATUS_SUCCESS 0
+#define HSMA_STATUS_INVALID_SIZE 1    /* negative size, leading dimension too small, overlapping outputs */
+#define HSMA_STATUS_INVALID_POINTER 2 /* NULL A, B or X where data must be read or written */
+#define HSMA_STATUS_NOT_SUPPORTED 3   /* shape outside what this entry point handles */
+#define HSMA_STATUS_ALLOC_FAILED 4    /* workspace allocation failed */
+#define HSMA_STATUS_HIP_ERROR 5       /* a HIP runtime call or kernel launch failed */
+#define HSMA_STATUS_INVALID_VALUE 6   /* bad option value */
+
+typedef struct { float re, im; } hsma_float_complex;
+typedef struct { double re, im; } hsma_double_complex;
+
+/* Element-type codes used by the helpers below. */
+#define HSMA_DTYPE_F32 0
+#define HSMA_DTYPE_F64 1
+#define HSMA_DTYPE_C64 2
+#define HSMA_DTYPE_C128 3
+
+/*
+ * hsma_trsm_{s,d,c,z}: one m x m system with n right-hand sides.
+ *   m     order of A (m >= 0); n: number of columns of B (n >= 0)
+ *   alpha scalar applied to B before the solve
+ *   A     device pointer, lda >= max(1, m); read-only, lower triangle only
+ *   B     device pointer, ldb >= max(1, m); on return holds X
+ * Errors: INVALID_SIZE, INVALID_POINTER (A or B NULL with m*n > 0),
+ *         ALLOC_FAILED, HIP_ERROR.
+ */
+hsma_status hsma_trsm_s(int64_t m, int64_t n, float alpha, const float *A, int64_t lda,
+                        float *B, int64_t ldb, void *stream);
+hsma_status hsma_trsm_d(int64_t m, int64_t n, double alpha, const double *A, int64_t lda,
+                        double *B, int64_t ldb, void *stream);
+hsma_status hsma_trsm_c(int64_t m, int64_t n, hsma_float_complex alpha,
+                        const hsma_float_complex *A, int64_t lda, hsma_float_complex *B,
+                        int64_t ldb, void *stream);
+hsma_status hsma_trsm_z(int64_t m, int64_t n, hsma_double_complex alpha,
+                        const hsma_double_complex *A, int64_t lda, hsma_double_complex *B,
+                        int64_t ldb, void *stream);
+
+/*
+ * hsma_trsm_strided_batched_{s,d,c,z}: batch_count independent systems;
+ * problem b uses A + b*strideA and B + b*strideB (strides in elements).
+ * strideA == 0 shares one A across the batch. B blocks must not overlap:
+ * strideB >= ldb*n when batch_count > 1 (else INVALID_SIZE).
+ * m <= 64 runs as one launch over the whole batch (the pages' small regime);
+ * larger m runs the blocked solver once per problem.
+ */
+hsma_status hsma_trsm_strided_batched_s(int64_t m, int64_t n, float alpha, const float *A,
+                                        int64_t lda, int64_t strideA, float *B, int64_t ldb,
+                                        int64_t strideB, int64_t batch_count, void *stream);
+hsma_status hsma_trsm_strided_batched_d(int64_t m, int64_t n, double alpha, const double *A,
+                                        int64_t lda, int64_t strideA, double *B, int64_t ldb,
+                                        int64_t strideB, int64_t batch_count, void *stream);
+hsma_status hsma_trsm_strided_batched_c(int64_t m, int64_t n, hsma_float_complex alpha,
+                                        const hsma_float_complex *A, int64_t lda, int64_t strideA,
+                                        hsma_float_complex *B, int64_t ldb, int64_t strideB,
+                                        int64_t batch_count, void *stream);
+hsma_status hsma_trsm_strided_batched_z(int64_t m, int64_t n, hsma_double_complex alpha,
+                                        const hsma_double_complex *A, int64_t lda, int64_t strideA,
+                                        hsma_double_complex *B, int64_t ldb, int64_t strideB,
+                                        int64_t batch_count, void *stream);
+
+/*
+ * hsma_solve_tri_f32: the ggml SOLVE_TRI operation (llama.cpp PR #17457,
+ * "SOLVE_TRI CUDA kernel for small matrices"): for every batch index
+ * (i2, i3) in [0, ne02) x [0, ne03), solve A X = B with A n x n lower
+ * triangular and B, X n x k, out of place.
+ * Layout is ggml's, row-major with the column index fastest:
+ *   A(i, j) = A[i*sA1 + j + i2*sA2 + i3*sA3]
+ *   B(i, c) = B[i*sB1 + c + i2*sB2 + i3*sB3]
+ *   X(i, c) = X[i*sX1 + c + i2*sX2 + i3*sX3]
+ * Strides are in elements (floats), as the PR's reviewers asked. B is
+ * read-only; X must not overlap A or B.
+ * n <= 64 (any k); larger n returns NOT_SUPPORTED, as the PR's kernel
+ * reports for the [128,128,4,1] case.
+ */
+hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float *B, float *X,
+                               int64_t ne02, int64_t ne03, int64_t sA1, int64_t sA2, int64_t sA3,
+                               int64_t sB1, int64_t sB2, int64_t sB3, int64_t sX1, int64_t sX2,
+                               int64_t sX3, void *stream);
+
+/*
+ * Options for the *_ex entry points (a NULL opts means all defaults).
+ *   nb    outer block size N_B of the blocked path (0: from the built-in
+ *         table); must be a multiple of 16 in [16, 1024]
+ *   ib    inner block size I_B of the diagonal inversion (0: nb/8); must
+ *         divide nb, and nb/ib <= 64
+ *   path  HSMA_PATH_AUTO, HSMA_PATH_SMALL (requires m <= 64) or
+ *         HSMA_PATH_BLOCKED (any m >= 1)
+ * Bad values return INVALID_VALUE.
+ */
+#define HSMA_PATH_AUTO 0
+#define HSMA_PATH_SMALL 1
+#define HSMA_PATH_BLOCKED 2
+typedef struct {
+    int32_t nb;
+    int32_t ib;
+    int32_t path;
+} hsma_trsm_opts;
+
+hsma_status hsma_trsm_ex_s(int64_t m, int64_t n, float alpha, const float *A, int64_t lda,
+                           float *B, int64_t ldb, const hsma_trsm_opts *opts, void *stream);
+hsma_status hsma_trsm_ex_d(int64_t m, int64_t n, double alpha, const double *A, int64_t lda,
+                           double *B, int64_t ldb, const hsma_trsm_opts *opts, void *stream);
+hsma_status hsma_trsm_ex_c(int64_t m, int64_t n, hsma_float_complex alpha,
+                           const hsma_float_complex *A, int64_t lda, hsma_float_complex *B,
+                           int64_t ldb, const hsma_trsm_opts *opts, void *stream);
+hsma_status hsma_trsm_ex_z(int64_t m, int64_t n, hsma_double_complex alpha,
+                           const hsma_double_complex *A, int64_t lda, hsma_double_complex *B,
+                           int64_t ldb, const hsma_trsm_opts *opts, void *stream);
+
+/*
+ * Building blocks of the blocked path, exported so that each step can be
+ * checked on its own.
+ *
+ * hsma_diag_inv_{s,d,c,z}: inverts every diagonal block of the lower
+ * triangle of A (HSMA-TRSM paper, blocked section: the diagonal blocks D_t
+ * are independent and are inverted in parallel, each by substitution against
+ * identity tiles E_j of width ib). Block t covers rows/columns
+ * [t*nb, min(m, (t+1)*nb)). invA receives ceil(m/nb) blocks of nb x nb,
+ * block t at invA + t*nb*nb, column-major with leading dimension nb; entries
+ * above the diagonal, and rows/columns beyond m in the last block, are
+ * written as exact zeros (the padded part of the last block holds the
+ * identity on its diagonal). nb, ib as in hsma_trsm_opts (0 = defaults).
+ */
+hsma_status hsma_diag_inv_s(int64_t m, int32_t nb, int32_t ib, const float *A, int64_t lda,
+                            float *invA, void *stream);
+hsma_status hsma_diag_inv_d(int64_t m, int32_t nb, int32_t ib, const double *A, int64_t lda,
+                            double *invA, void *stream);
+hsma_status hsma_diag_inv_c(int64_t m, int32_t nb, int32_t ib, const hsma_float_complex *A,
+                            int64_t lda, hsma_float_complex *invA, void *stream);
+hsma_status hsma_diag_inv_z(int64_t m, int32_t nb, int32_t ib, const hsma_double_complex *A,
+                            int64_t lda, hsma_double_complex *invA, void *stream);
+
+/*
+ * hsma_gemm_{s,d,c,z}: C = beta*C + alpha*op(A)*B with A M x K, B K x N,
+ * C M x N, all column-major, on the matrix cores (the update of the trailing
+ * rows and the multiply by an inverted diagonal block in the blocked path).
+ * alpha and beta are real, beta must be 0 or 1 (beta == 0: C is not read).
+ * a_lower != 0 declares A lower triangular with M == K: the kernel then skips
+ * the zero tiles above the diagonal and treats those entries as exact zeros
+ * (it never reads them). C must not overlap A or B.
+ */
+hsma_status hsma_gemm_s(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                        const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                        int32_t a_lower, void *stream);
+hsma_status hsma_gemm_d(int64_t M, int64_t N, int64_t K, double alpha, const double *A,
+                        int64_t lda, const double *B, int64_t ldb, double beta, double *C,
+                        int64_t ldc, int32_t a_lower, void *stream);
+hsma_status hsma_gemm_c(int64_t M, int64_t N, int64_t K, float alpha, const hsma_float_complex *A,
+                        int64_t lda, const hsma_float_complex *B, int64_t ldb, float beta,
+                        hsma_float_complex *C, int64_t ldc, int32_t a_lower, void *stream);
+hsma_status hsma_gemm_z(int64_t M, int64_t N, int64_t K, double alpha,
+                        const hsma_double_complex *A, int64_t lda, const hsma_double_complex *B,
+                        int64_t ldb, double beta, hsma_double_complex *C, int64_t ldc,
+                        int32_t a_lower, void *stream);
+
+/*
+ * hsma_trsm_block_size: the outer block size N_B the blocked path uses for
+ * an m x m problem of the given dtype (HSMA_DTYPE_*), from the built-in
+ * "size x dtype -> block" table by nearest tested size (HSMA-TRSM paper,
+ * adaptive blocking section). Returns 0 for m <= 64 (small path) and -1 for
+ * a bad dtype. The environment variable HSMA_NB, read once, overrides the
+ * table when set to a valid block size.
+ */
+int32_t hsma_trsm_block_size(int32_t dtype, int64_t m);
+
+/* Static, human-readable name of a status code. */
+const char *hsma_status_string(hsma_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSMA_TRSM_H */

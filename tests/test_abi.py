@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsma_trsm.h")
+
+
+@pytest.fixture(scope="module")
+def hs():
+    import triangular_solve_amd as hs
+    return hs
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsma_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(hs):
+    lib = ctypes.CDLL(hs.LIB_PATH)
+    names = declared_functions()
+    assert len(names) == 23
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(names) == hs.EXPORTS
+
+
+def test_status_strings(hs):
+    assert hs.hsma_status_string(0) == "success"
+    assert hs.hsma_status_string(hs.NOT_SUPPORTED) == "not supported"
+    assert hs.hsma_status_string(12345) == "unknown status"
+
+
+BAD = 0xDEAD000  # never dereferenced: every call below returns before any GPU work
+
+
+@pytest.mark.parametrize("t", ["f32", "f64", "c64", "c128"])
+def test_trsm_argument_checks(hs, t):
+    f = hs.entry("trsm", t)
+    assert f(-1, 4, 1, BAD, 4, BAD, 4, 0) == hs.INVALID_SIZE
+    assert f(4, -1, 1, BAD, 4, BAD, 4, 0) == hs.INVALID_SIZE
+    assert f(4, 4, 1, BAD, 3, BAD, 4, 0) == hs.INVALID_SIZE       # lda < m
+    assert f(4, 4, 1, BAD, 4, BAD, 3, 0) == hs.INVALID_SIZE       # ldb < m
+    assert f(0, 4, 1, BAD, 0, BAD, 0, 0) == hs.INVALID_SIZE       # lda < 1
+    assert f(0, 4, 1, None, 1, None, 1, 0) == hs.SUCCESS          # empty: nothing touched
+    assert f(4, 0, 1, None, 4, None, 4, 0) == hs.SUCCESS
+    assert f(4, 4, 1, BAD, 4, None, 4, 0) == hs.INVALID_POINTER   # B NULL
+    assert f(4, 4, 1, None, 4, BAD, 4, 0) == hs.INVALID_POINTER   # A NULL, alpha != 0
+
+
+@pytest.mark.parametrize("t", ["f32", "c128"])
+def test_batched_argument_checks(hs, t):
+    f = hs.entry("strided_batched", t)
+    assert f(8, 8, 1, BAD, 8, 64, BAD, 8, 63, 2, 0) == hs.INVALID_SIZE   # overlapping B blocks
+    assert f(8, 8, 1, BAD, 8, -1, BAD, 8, 64, 2, 0) == hs.INVALID_SIZE
+    assert f(8, 8, 1, BAD, 8, 64, BAD, 8, 64, -1, 0) == hs.INVALID_SIZE
+    assert f(8, 8, 1, BAD, 8, 64, BAD, 8, 64, 0, 0) == hs.SUCCESS
+    assert f(8, 8, 1, None, 8, 0, BAD, 8, 64, 3, 0) == hs.INVALID_POINTER
+
+
+def test_ex_option_checks(hs):
+    f = hs.entry("ex", "f64")
+    assert f(100, 4, 1, BAD, 100, BAD, 100, {"path": 7}, 0) == hs.INVALID_VALUE
+    assert f(100, 4, 1, BAD, 100, BAD, 100, {"path": hs.PATH_SMALL}, 0) == hs.INVALID_VALUE
+    assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 100}, 0) == hs.INVALID_VALUE   # not a multiple of 16
+    assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 2048}, 0) == hs.INVALID_VALUE
+    assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 128, "ib": 3}, 0) == hs.INVALID_VALUE
+    assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 128, "ib": 1}, 0) == hs.INVALID_VALUE  # nb/ib > 64
+    assert hs.entry("ex", "c128")(600, 4, 1, BAD, 600, BAD, 600, {"nb": 1024}, 0) == hs.INVALID_VALUE
+
+
+def test_solve_tri_checks(hs):
+    f = hs.hsma_solve_tri_f32
+    # the PR's [128,128,4,1] / [8,128,4,1] case is not supported by this entry
+    assert f(128, 8, BAD, BAD, BAD, 4, 1, 128, 128 * 128, 4 * 128 * 128, 8, 8 * 128, 4 * 8 * 128,
+             8, 8 * 128, 4 * 8 * 128, 0) == hs.NOT_SUPPORTED
+    assert f(64, 6, BAD, BAD, BAD, 4, 2, 63, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.INVALID_SIZE
+    assert f(64, 6, BAD, None, BAD, 4, 2, 64, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.INVALID_POINTER
+    assert f(64, 0, None, None, None, 4, 2, 64, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.SUCCESS
+    assert f(-1, 6, BAD, BAD, BAD, 4, 2, 64, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.INVALID_SIZE
+
+
+def test_gemm_and_diag_inv_checks(hs):
+    g = hs.entry("gemm", "f32")
+    assert g(4, 4, 5, 1, BAD, 4, BAD, 5, 0, BAD, 4, 1, 0) == hs.INVALID_SIZE   # lower needs M == K
+    assert g(4, 4, 4, 1, BAD, 4, BAD, 4, 0.5, BAD, 4, 0, 0) == hs.INVALID_VALUE
+    assert g(4, 4, 4, 1, BAD, 3, BAD, 4, 0, BAD, 4, 0, 0) == hs.INVALID_SIZE
+    assert g(0, 4, 4, 1, None, 1, None, 4, 0, None, 1, 0, 0) == hs.SUCCESS
+    d = hs.entry("diag_inv", "f64")
+    assert d(100, 100, 0, BAD, 100, BAD, 0) == hs.INVALID_VALUE
+    assert d(100, 128, 1, BAD, 100, BAD, 0) == hs.INVALID_VALUE
+    assert d(100, 128, 16, BAD, 99, BAD, 0) == hs.INVALID_SIZE
+    assert d(100, 128, 16, None, 100, BAD, 0) == hs.INVALID_POINTER
+    assert d(0, 128, 16, None, 1, None, 0) == hs.SUCCESS
+
+
+def test_block_size_table(hs):
+    for code in range(4):
+        assert hs.hsma_trsm_block_size(code, 64) == 0
+        for m in (65, 100, 1000, 1024, 3000, 8192, 16384, 50000):
+            nb = hs.hsma_trsm_block_size(code, m)
+            assert nb % 16 == 0 and 16 <= nb <= 1024
+            assert nb <= ((m + 15) // 16) * 16
+    assert hs.hsma_trsm_block_size(7, 100) == -1

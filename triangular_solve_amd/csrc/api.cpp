@@ -1,0 +1,388 @@
+// api.cpp - the C ABI (include/hsma_trsm.h): argument checks, quick returns,
+// path dispatch and the blocked path's workspace.
+//
+// Dispatch follows the HSMA-TRSM pages' size x dtype strategy (news summary,
+// "One framework, several paths"; paper, small-scale section): m <= 64 is
+// solved directly on chip, larger m by the blocked solver whose outer block
+// N_B comes from a "size x dtype -> block" table with nearest-size lookup
+// (paper, adaptive blocking section).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/hsma_trsm.h"
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace hsma {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Block-size table: tested sizes m_i and the best N_B at each, per dtype.
+// Lookup takes the tested size nearest to m on a log scale (ties go to the
+// smaller size), then clamps N_B to m rounded up to a multiple of 16.
+
+struct NbEntry {
+    int64_t m;
+    int nb;
+};
+
+#include "nb_table.inc"
+
+int table_lookup(int dtype, int64_t m)
+{
+    const NbEntry *tab = nullptr;
+    int len = 0;
+    switch (dtype) {
+    case 0: tab = kNbF32; len = (int)(sizeof(kNbF32) / sizeof(kNbF32[0])); break;
+    case 1: tab = kNbF64; len = (int)(sizeof(kNbF64) / sizeof(kNbF64[0])); break;
+    case 2: tab = kNbC64; len = (int)(sizeof(kNbC64) / sizeof(kNbC64[0])); break;
+    case 3: tab = kNbC128; len = (int)(sizeof(kNbC128) / sizeof(kNbC128[0])); break;
+    default: return -1;
+    }
+    const double lm = std::log2((double)m);
+    int best = 0;
+    double bd = 1e300;
+    for (int i = 0; i < len; ++i) {
+        const double d = std::fabs(lm - std::log2((double)tab[i].m));
+        if (d < bd - 1e-12) { bd = d; best = i; }
+    }
+    return tab[best].nb;
+}
+
+bool valid_nb(int64_t nb) { return nb >= 16 && nb <= 1024 && nb % 16 == 0; }
+
+int env_nb()
+{
+    static int value = -1;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        const char *s = std::getenv("HSMA_NB");
+        if (s) {
+            char *end = nullptr;
+            const long v = std::strtol(s, &end, 10);
+            if (end != s && valid_nb(v)) value = (int)v;
+        }
+    });
+    return value;
+}
+
+int max_nb_for(int dtype) { return dtype == 3 ? 512 : 1024; }
+
+int choose_nb(int dtype, int64_t m)
+{
+    int nb = env_nb();
+    if (nb <= 0) nb = table_lookup(dtype, m);
+    if (nb > max_nb_for(dtype)) nb = max_nb_for(dtype);
+    const int64_t cap = ((m + 15) / 16) * 16;
+    if (nb > cap) nb = (int)(cap < 16 ? 16 : cap);
+    return nb;
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename T>
+T from_abi(T v) { return v; }
+inline c32 from_abi(hsma_float_complex v) { return {v.re, v.im}; }
+inline c64 from_abi(hsma_double_complex v) { return {v.re, v.im}; }
+
+hsma_status hip_status(hipError_t e)
+{
+    return e == hipSuccess ? HSMA_STATUS_SUCCESS : HSMA_STATUS_HIP_ERROR;
+}
+
+int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
+{
+    if (!o) return HSMA_STATUS_SUCCESS;
+    if (o->path < HSMA_PATH_AUTO || o->path > HSMA_PATH_BLOCKED) return HSMA_STATUS_INVALID_VALUE;
+    if (o->path == HSMA_PATH_SMALL && m > 64) return HSMA_STATUS_INVALID_VALUE;
+    if (o->nb != 0 && (!valid_nb(o->nb) || o->nb > max_nb_for(dtype)))
+        return HSMA_STATUS_INVALID_VALUE;
+    if (o->ib != 0) {
+        const int nb = o->nb != 0 ? o->nb : 0;
+        if (o->ib < 1) return HSMA_STATUS_INVALID_VALUE;
+        if (nb != 0 && (nb % o->ib != 0 || nb / o->ib > 64)) return HSMA_STATUS_INVALID_VALUE;
+    }
+    return HSMA_STATUS_SUCCESS;
+}
+
+// Small path on column-major storage, in place.
+template <typename T>
+hipError_t small_path(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
+                      T *B, int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s)
+{
+    // The lane-per-column kernel needs the full 64 rows and enough columns to
+    // fill a wavefront; otherwise the lane-per-row kernel.
+    if (m == 64 && n >= 32)
+        return small_colane<T>(n, alpha, A, lda, strideA, B, ldb, strideB, batch, s);
+    return small_rowlane<T>(A, 1, lda, strideA, 0, B, 1, ldb, strideB, 0, B, 1, ldb, strideB, 0,
+                            m, n, batch, 1, alpha, s);
+}
+
+template <typename T>
+hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
+                      T *B, int64_t ldb, int64_t strideB, int64_t batch,
+                      const hsma_trsm_opts *opts, void *stream)
+{
+    constexpr int dt = traits<T>::dtype;
+    if (m < 0 || n < 0 || batch < 0) return HSMA_STATUS_INVALID_SIZE;
+    if (lda < imax(1, m) || ldb < imax(1, m)) return HSMA_STATUS_INVALID_SIZE;
+    if (strideA < 0 || strideB < 0) return HSMA_STATUS_INVALID_SIZE;
+    if (batch > 1 && strideB < ldb * n) return HSMA_STATUS_INVALID_SIZE;
+    const hsma_status os = check_opts(opts, dt, m);
+    if (os != HSMA_STATUS_SUCCESS) return os;
+    if (m == 0 || n == 0 || batch == 0) return HSMA_STATUS_SUCCESS;
+    if (!B) return HSMA_STATUS_INVALID_POINTER;
+    hipStream_t s = (hipStream_t)stream;
+    if (is_zero(alpha)) return hip_status(scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, true, s));
+    if (!A) return HSMA_STATUS_INVALID_POINTER;
+
+    const int path = opts ? opts->path : HSMA_PATH_AUTO;
+    const bool small = path == HSMA_PATH_SMALL || (path == HSMA_PATH_AUTO && m <= 64);
+    if (small) return hip_status(small_path<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
+
+    // Blocked path.
+    int nb = (opts && opts->nb) ? opts->nb : choose_nb(dt, m);
+    if (!(opts && opts->nb)) {
+        const int64_t cap = ((m + 15) / 16) * 16;
+        if (nb > cap) nb = (int)cap;
+    }
+    int ib = (opts && opts->ib) ? opts->ib : (nb / 8 > 0 ? nb / 8 : 1);
+    if (nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
+
+    const int64_t welems = blocked_workspace_elems(m, n, nb);
+    void *work = nullptr;
+    if (hipMallocAsync(&work, (size_t)welems * sizeof(T), s) != hipSuccess || !work) {
+        (void)hipGetLastError();
+        return HSMA_STATUS_ALLOC_FAILED;
+    }
+    hipError_t e = hipSuccess;
+    if (!is_one(alpha)) e = scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, false, s);
+    for (int64_t b = 0; b < batch && e == hipSuccess; ++b)
+        e = blocked_solve<T>(m, n, nb, ib, A + b * strideA, lda, B + b * strideB, ldb, (T *)work, s);
+    const hipError_t ef = hipFreeAsync(work, s);
+    if (e != hipSuccess || ef != hipSuccess) return HSMA_STATUS_HIP_ERROR;
+    return HSMA_STATUS_SUCCESS;
+}
+
+template <typename T>
+hsma_status diag_inv_impl(int64_t m, int32_t nb, int32_t ib, const T *A, int64_t lda, T *invA,
+                          void *stream)
+{
+    constexpr int dt = traits<T>::dtype;
+    if (m < 0 || lda < imax(1, m)) return HSMA_STATUS_INVALID_SIZE;
+    if (nb == 0) nb = choose_nb(dt, m > 64 ? m : 65);
+    if (!valid_nb(nb) || nb > max_nb_for(dt)) return HSMA_STATUS_INVALID_VALUE;
+    if (ib == 0) ib = nb / 8;
+    if (ib < 1 || nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
+    if (m == 0) return HSMA_STATUS_SUCCESS;
+    if (!A || !invA) return HSMA_STATUS_INVALID_POINTER;
+    return hip_status(diag_invert<T>(m, nb, ib, A, lda, invA, (hipStream_t)stream));
+}
+
+template <typename T>
+hsma_status gemm_impl(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
+                      int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
+                      int64_t ldc, int32_t a_lower, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0) return HSMA_STATUS_INVALID_SIZE;
+    if (lda < imax(1, M) || ldb < imax(1, K) || ldc < imax(1, M)) return HSMA_STATUS_INVALID_SIZE;
+    if (a_lower && M != K) return HSMA_STATUS_INVALID_SIZE;
+    if (!(beta == 0 || beta == 1)) return HSMA_STATUS_INVALID_VALUE;
+    if (M == 0 || N == 0) return HSMA_STATUS_SUCCESS;
+    if (!C || (K > 0 && (!A || !B))) return HSMA_STATUS_INVALID_POINTER;
+    return hip_status(gemm<T>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower != 0,
+                              (hipStream_t)stream));
+}
+
+}  // namespace
+}  // namespace hsma
+
+using namespace hsma;
+
+#define HSMA_NOEXCEPT(expr)                                                                        \
+    try {                                                                                          \
+        return expr;                                                                               \
+    } catch (...) {                                                                                \
+        return HSMA_STATUS_HIP_ERROR;                                                              \
+    }
+
+extern "C" {
+
+hsma_status hsma_trsm_s(int64_t m, int64_t n, float alpha, const float *A, int64_t lda, float *B,
+                        int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<float>(m, n, alpha, A, lda, 0, B, ldb, 0, 1, nullptr, stream))
+}
+hsma_status hsma_trsm_d(int64_t m, int64_t n, double alpha, const double *A, int64_t lda,
+                        double *B, int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<double>(m, n, alpha, A, lda, 0, B, ldb, 0, 1, nullptr, stream))
+}
+hsma_status hsma_trsm_c(int64_t m, int64_t n, hsma_float_complex alpha,
+                        const hsma_float_complex *A, int64_t lda, hsma_float_complex *B,
+                        int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<c32>(m, n, from_abi(alpha), (const c32 *)A, lda, 0, (c32 *)B, ldb, 0,
+                                 1, nullptr, stream))
+}
+hsma_status hsma_trsm_z(int64_t m, int64_t n, hsma_double_complex alpha,
+                        const hsma_double_complex *A, int64_t lda, hsma_double_complex *B,
+                        int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<c64>(m, n, from_abi(alpha), (const c64 *)A, lda, 0, (c64 *)B, ldb, 0,
+                                 1, nullptr, stream))
+}
+
+hsma_status hsma_trsm_strided_batched_s(int64_t m, int64_t n, float alpha, const float *A,
+                                        int64_t lda, int64_t strideA, float *B, int64_t ldb,
+                                        int64_t strideB, int64_t batch_count, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<float>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch_count,
+                                   nullptr, stream))
+}
+hsma_status hsma_trsm_strided_batched_d(int64_t m, int64_t n, double alpha, const double *A,
+                                        int64_t lda, int64_t strideA, double *B, int64_t ldb,
+                                        int64_t strideB, int64_t batch_count, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<double>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch_count,
+                                    nullptr, stream))
+}
+hsma_status hsma_trsm_strided_batched_c(int64_t m, int64_t n, hsma_float_complex alpha,
+                                        const hsma_float_complex *A, int64_t lda, int64_t strideA,
+                                        hsma_float_complex *B, int64_t ldb, int64_t strideB,
+                                        int64_t batch_count, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<c32>(m, n, from_abi(alpha), (const c32 *)A, lda, strideA, (c32 *)B,
+                                 ldb, strideB, batch_count, nullptr, stream))
+}
+hsma_status hsma_trsm_strided_batched_z(int64_t m, int64_t n, hsma_double_complex alpha,
+                                        const hsma_double_complex *A, int64_t lda, int64_t strideA,
+                                        hsma_double_complex *B, int64_t ldb, int64_t strideB,
+                                        int64_t batch_count, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<c64>(m, n, from_abi(alpha), (const c64 *)A, lda, strideA, (c64 *)B,
+                                 ldb, strideB, batch_count, nullptr, stream))
+}
+
+hsma_status hsma_trsm_ex_s(int64_t m, int64_t n, float alpha, const float *A, int64_t lda,
+                           float *B, int64_t ldb, const hsma_trsm_opts *opts, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<float>(m, n, alpha, A, lda, 0, B, ldb, 0, 1, opts, stream))
+}
+hsma_status hsma_trsm_ex_d(int64_t m, int64_t n, double alpha, const double *A, int64_t lda,
+                           double *B, int64_t ldb, const hsma_trsm_opts *opts, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<double>(m, n, alpha, A, lda, 0, B, ldb, 0, 1, opts, stream))
+}
+hsma_status hsma_trsm_ex_c(int64_t m, int64_t n, hsma_float_complex alpha,
+                           const hsma_float_complex *A, int64_t lda, hsma_float_complex *B,
+                           int64_t ldb, const hsma_trsm_opts *opts, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<c32>(m, n, from_abi(alpha), (const c32 *)A, lda, 0, (c32 *)B, ldb, 0,
+                                 1, opts, stream))
+}
+hsma_status hsma_trsm_ex_z(int64_t m, int64_t n, hsma_double_complex alpha,
+                           const hsma_double_complex *A, int64_t lda, hsma_double_complex *B,
+                           int64_t ldb, const hsma_trsm_opts *opts, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_impl<c64>(m, n, from_abi(alpha), (const c64 *)A, lda, 0, (c64 *)B, ldb, 0,
+                                 1, opts, stream))
+}
+
+hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float *B, float *X,
+                               int64_t ne02, int64_t ne03, int64_t sA1, int64_t sA2, int64_t sA3,
+                               int64_t sB1, int64_t sB2, int64_t sB3, int64_t sX1, int64_t sX2,
+                               int64_t sX3, void *stream)
+{
+    try {
+        if (n < 0 || k < 0 || ne02 < 0 || ne03 < 0) return HSMA_STATUS_INVALID_SIZE;
+        if (n == 0 || k == 0 || ne02 == 0 || ne03 == 0) return HSMA_STATUS_SUCCESS;
+        if (n > 64) return HSMA_STATUS_NOT_SUPPORTED;
+        if (sA1 < n || sB1 < k || sX1 < k) return HSMA_STATUS_INVALID_SIZE;
+        if (sA2 < 0 || sA3 < 0 || sB2 < 0 || sB3 < 0 || sX2 < 0 || sX3 < 0)
+            return HSMA_STATUS_INVALID_SIZE;
+        if (!A || !B || !X) return HSMA_STATUS_INVALID_POINTER;
+        return hip_status(small_rowlane<float>(A, sA1, 1, sA2, sA3, B, sB1, 1, sB2, sB3, X, sX1, 1,
+                                               sX2, sX3, n, k, ne02, ne03, 1.0f,
+                                               (hipStream_t)stream));
+    } catch (...) {
+        return HSMA_STATUS_HIP_ERROR;
+    }
+}
+
+hsma_status hsma_diag_inv_s(int64_t m, int32_t nb, int32_t ib, const float *A, int64_t lda,
+                            float *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_impl<float>(m, nb, ib, A, lda, invA, stream))
+}
+hsma_status hsma_diag_inv_d(int64_t m, int32_t nb, int32_t ib, const double *A, int64_t lda,
+                            double *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_impl<double>(m, nb, ib, A, lda, invA, stream))
+}
+hsma_status hsma_diag_inv_c(int64_t m, int32_t nb, int32_t ib, const hsma_float_complex *A,
+                            int64_t lda, hsma_float_complex *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_impl<c32>(m, nb, ib, (const c32 *)A, lda, (c32 *)invA, stream))
+}
+hsma_status hsma_diag_inv_z(int64_t m, int32_t nb, int32_t ib, const hsma_double_complex *A,
+                            int64_t lda, hsma_double_complex *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_impl<c64>(m, nb, ib, (const c64 *)A, lda, (c64 *)invA, stream))
+}
+
+hsma_status hsma_gemm_s(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                        const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                        int32_t a_lower, void *stream)
+{
+    HSMA_NOEXCEPT(gemm_impl<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower, stream))
+}
+hsma_status hsma_gemm_d(int64_t M, int64_t N, int64_t K, double alpha, const double *A,
+                        int64_t lda, const double *B, int64_t ldb, double beta, double *C,
+                        int64_t ldc, int32_t a_lower, void *stream)
+{
+    HSMA_NOEXCEPT(gemm_impl<double>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower, stream))
+}
+hsma_status hsma_gemm_c(int64_t M, int64_t N, int64_t K, float alpha, const hsma_float_complex *A,
+                        int64_t lda, const hsma_float_complex *B, int64_t ldb, float beta,
+                        hsma_float_complex *C, int64_t ldc, int32_t a_lower, void *stream)
+{
+    HSMA_NOEXCEPT(gemm_impl<c32>(M, N, K, alpha, (const c32 *)A, lda, (const c32 *)B, ldb, beta,
+                                 (c32 *)C, ldc, a_lower, stream))
+}
+hsma_status hsma_gemm_z(int64_t M, int64_t N, int64_t K, double alpha,
+                        const hsma_double_complex *A, int64_t lda, const hsma_double_complex *B,
+                        int64_t ldb, double beta, hsma_double_complex *C, int64_t ldc,
+                        int32_t a_lower, void *stream)
+{
+    HSMA_NOEXCEPT(gemm_impl<c64>(M, N, K, alpha, (const c64 *)A, lda, (const c64 *)B, ldb, beta,
+                                 (c64 *)C, ldc, a_lower, stream))
+}
+
+int32_t hsma_trsm_block_size(int32_t dtype, int64_t m)
+{
+    if (dtype < 0 || dtype > 3) return -1;
+    if (m <= 64) return 0;
+    return choose_nb(dtype, m);
+}
+
+const char *hsma_status_string(hsma_status status)
+{
+    switch (status) {
+    case HSMA_STATUS_SUCCESS: return "success";
+    case HSMA_STATUS_INVALID_SIZE: return "invalid size";
+    case HSMA_STATUS_INVALID_POINTER: return "invalid pointer";
+    case HSMA_STATUS_NOT_SUPPORTED: return "not supported";
+    case HSMA_STATUS_ALLOC_FAILED: return "workspace allocation failed";
+    case HSMA_STATUS_HIP_ERROR: return "HIP error";
+    case HSMA_STATUS_INVALID_VALUE: return "invalid value";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

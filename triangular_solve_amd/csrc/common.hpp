@@ -1,0 +1,136 @@
+// common.hpp - element types and arithmetic shared by the library's kernels.
+//
+// Four element types: float, double and the two complex types, each complex
+// value stored as an interleaved (re, im) pair exactly like
+// hsma_float_complex / hsma_double_complex in the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace hsma {
+
+template <typename R>
+struct cplx {
+    R re, im;
+};
+
+using c32 = cplx<float>;
+using c64 = cplx<double>;
+
+template <typename T> struct traits;
+template <> struct traits<float> {
+    using real = float;
+    static constexpr bool is_complex = false;
+    static constexpr int dtype = 0;
+};
+template <> struct traits<double> {
+    using real = double;
+    static constexpr bool is_complex = false;
+    static constexpr int dtype = 1;
+};
+template <> struct traits<c32> {
+    using real = float;
+    static constexpr bool is_complex = true;
+    static constexpr int dtype = 2;
+};
+template <> struct traits<c64> {
+    using real = double;
+    static constexpr bool is_complex = true;
+    static constexpr int dtype = 3;
+};
+
+// ---- scalar arithmetic, written once for real and complex ------------------
+
+__host__ __device__ inline float zero_of(float) { return 0.f; }
+__host__ __device__ inline double zero_of(double) { return 0.0; }
+__host__ __device__ inline c32 zero_of(c32) { return {0.f, 0.f}; }
+__host__ __device__ inline c64 zero_of(c64) { return {0.0, 0.0}; }
+
+__host__ __device__ inline bool is_zero(float a) { return a == 0.f; }
+__host__ __device__ inline bool is_zero(double a) { return a == 0.0; }
+__host__ __device__ inline bool is_zero(c32 a) { return a.re == 0.f && a.im == 0.f; }
+__host__ __device__ inline bool is_zero(c64 a) { return a.re == 0.0 && a.im == 0.0; }
+
+__host__ __device__ inline bool is_one(float a) { return a == 1.f; }
+__host__ __device__ inline bool is_one(double a) { return a == 1.0; }
+__host__ __device__ inline bool is_one(c32 a) { return a.re == 1.f && a.im == 0.f; }
+__host__ __device__ inline bool is_one(c64 a) { return a.re == 1.0 && a.im == 0.0; }
+
+__device__ inline float fmaR(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ inline double fmaR(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
+__device__ inline float mul(float a, float b) { return a * b; }
+__device__ inline double mul(double a, double b) { return a * b; }
+template <typename R>
+__device__ inline cplx<R> mul(cplx<R> a, cplx<R> b)
+{
+    return {fmaR(a.re, b.re, -a.im * b.im), fmaR(a.re, b.im, a.im * b.re)};
+}
+
+// w - a*x, as fused multiply-adds.
+__device__ inline float fms(float w, float a, float x) { return __builtin_fmaf(-a, x, w); }
+__device__ inline double fms(double w, double a, double x) { return __builtin_fma(-a, x, w); }
+template <typename R>
+__device__ inline cplx<R> fms(cplx<R> w, cplx<R> a, cplx<R> x)
+{
+    cplx<R> r;
+    r.re = fmaR(-a.re, x.re, w.re);
+    r.re = fmaR(a.im, x.im, r.re);
+    r.im = fmaR(-a.re, x.im, w.im);
+    r.im = fmaR(-a.im, x.re, r.im);
+    return r;
+}
+
+// 1/d with IEEE division (complex: conj(d) / |d|^2).
+__device__ inline float recip(float d) { return 1.0f / d; }
+__device__ inline double recip(double d) { return 1.0 / d; }
+template <typename R>
+__device__ inline cplx<R> recip(cplx<R> d)
+{
+    const R den = d.re * d.re + d.im * d.im;
+    return {d.re / den, -d.im / den};
+}
+
+inline float host_recip(float a) { return 1.0f / a; }
+inline double host_recip(double a) { return 1.0 / a; }
+template <typename R>
+inline cplx<R> host_recip(cplx<R> d)
+{
+    const R den = d.re * d.re + d.im * d.im;
+    return {d.re / den, -d.im / den};
+}
+
+// ---- cross-lane broadcast of a wave-uniform lane index (v_readlane) --------
+
+__device__ inline float readlane(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ inline double readlane(double v, int lane)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffff), lane);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+template <typename R>
+__device__ inline cplx<R> readlane(cplx<R> v, int lane)
+{
+    return {readlane(v.re, lane), readlane(v.im, lane)};
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E), so
+// that register-array indices inside f are constants after inlining.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+}  // namespace hsma

@@ -1,0 +1,47 @@
+// internal.hpp - launchers shared between the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace hsma {
+
+// Small regime, lane = row (any m <= 64, any strides; X may alias B).
+template <typename T>
+hipError_t small_rowlane(const T *A, int64_t sai, int64_t saj, int64_t sa2, int64_t sa3,
+                         const T *B, int64_t sbi, int64_t sbj, int64_t sb2, int64_t sb3,
+                         T *X, int64_t sxi, int64_t sxj, int64_t sx2, int64_t sx3,
+                         int64_t m, int64_t n, int64_t ne02, int64_t ne03, T alpha, hipStream_t s);
+
+// Small regime, lane = right-hand-side column (m == 64, column-major, in place).
+template <typename T>
+hipError_t small_colane(int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA, T *B,
+                        int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s);
+
+// B := alpha*B, or B := 0 when set_zero (column-major, batched).
+template <typename T>
+hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB, int64_t batch,
+                        T alpha, bool set_zero, hipStream_t s);
+
+// Blocked regime: inversion of all diagonal blocks of size nb (inner block ib).
+template <typename T>
+hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
+                       hipStream_t s);
+
+// C = beta*C + alpha*A*B on the matrix cores (beta in {0, 1}); a_lower: A is
+// lower triangular (M == K) and its upper tiles are skipped.
+template <typename T>
+hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
+                int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
+                int64_t ldc, bool a_lower, hipStream_t s);
+
+// Whole blocked solve of one problem (B already scaled by alpha), with a
+// caller-provided workspace of blocked_workspace_elems(m, n, nb) elements.
+int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb);
+template <typename T>
+hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
+                         int64_t ldb, T *work, hipStream_t s);
+
+}  // namespace hsma
