@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X triangular-solve library (left, lower, no-transpose,
+non-unit TRSM), printing one JSON line.
+
+Default workload (one "step"): the batched small regime, 4096 column-major
+64 x 64 systems with 64 right-hand sides each, solved in f32, f64, c64 and
+c128 (four launches of the library's small-regime kernel, one per dtype).
+value = LAPACK-count GFLOPS of the whole step (m^2 n per real problem,
+4 m^2 n per complex one). Inputs are resident in HBM before timing starts;
+every step solves distinct copies of A and B (a ring larger than the 256 MB
+MALL), so no step reads another step's data from cache.
+
+The same line carries the blocked regime at m = n = 8192 (one solve per
+dtype, LAPACK GFLOPS and the MFMA-peak fraction), the SOLVE_TRI shape
+(8 systems of 64 x 64 with 6 right-hand sides, ggml layout, us per call), the
+roofline of the dominant kernel, and the CPU oracle timed on the same step.
+
+  python bench.py [--steps K] [--warmup W] [--no-blocked] [--no-cpu]
+  python bench.py --workload blocked --m 16384 --dtypes f32,f64,c128
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TRSM GFLOPS (m=64 batched; m=8192/16384 blocked) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "c64": 157.3, "f64": 78.6, "c128": 78.6}
+ITEMSIZE = {"f32": 4, "f64": 8, "c64": 8, "c128": 16}
+DTYPES = ["f32", "f64", "c64", "c128"]
+SEED_CFG0, SEED_CFG1, SEED_CFG3 = 0x5EED0000, 0x5EED0001, 0x5EED0003
+
+
+def lapack_flops(dtype, m, n):
+    """LAPACK operation count of one m x m TRSM with n right-hand sides."""
+    return (4 if dtype.startswith("c") else 1) * m * m * n
+
+
+def small_bytes(dtype, m, n):
+    """Algorithmic HBM bytes of one in-place small solve: triangle of A, read B, write X."""
+    return (m * (m + 1) // 2 + 2 * m * n) * ITEMSIZE[dtype]
+
+
+def ggml_bytes(n, k, nbatch, itemsize):
+    """test-backend-ops byte count for SOLVE_TRI: full A + B + X."""
+    return (n * n + 2 * n * k) * nbatch * itemsize
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+
+def batched_inputs(dtype, m, n, batch, seed):
+    import synth
+    A = synth.tri(dtype, m, batch, seed=seed, offdiag_div=m)
+    B = synth.rhs(dtype, m, n, batch, seed=seed + 1)
+    return A, B
+
+
+def bench_batched(hs, torch, steps, warmup, m=64, n=64, batch=4096, check=True):
+    """Timed steps of the batched small regime over all four dtypes."""
+    stream = torch.cuda.current_stream()
+    nslot = 2  # each slot (all dtypes) is > 1 GB, so alternating slots defeats the MALL
+    host, slots = {}, {}
+    for dt in DTYPES:
+        A, B = batched_inputs(dt, m, n, batch, SEED_CFG1)
+        host[dt] = (A, B)
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        slots[dt] = [(dA.clone(), dB.clone()) for _ in range(nslot)]
+    f = {dt: hs.entry("strided_batched", dt) for dt in DTYPES}
+
+    def launch(dt, slot):
+        dA, dB = slots[dt][slot]
+        st = f[dt](m, n, 1.0, dA, m, m * m, dB, m, m * n, batch, stream)
+        if st != hs.SUCCESS:
+            raise hs.HsmaError(st, "strided_batched_" + dt)
+
+    parity = {}
+    if check:
+        import oracle
+        for dt in DTYPES:
+            launch(dt, 0)
+        torch.cuda.synchronize()
+        for dt in DTYPES:
+            A, B = host[dt]
+            sel = np.arange(0, batch, max(1, batch // 64))          # 64 problems, spread out
+            Xg = slots[dt][0][1].cpu().numpy()[sel][:, :, :m].transpose(0, 2, 1)
+            Xo = oracle.trsm(A[sel][:, :, :m].transpose(0, 2, 1), B[sel][:, :, :m].transpose(0, 2, 1))
+            num = np.sqrt(np.sum(np.abs(Xg.astype(Xo.dtype) - Xo) ** 2, axis=(1, 2)))
+            den = np.sqrt(np.sum(np.abs(Xo) ** 2, axis=(1, 2)))
+            parity[dt] = float(np.max(num / den))
+            slots[dt][0][1].copy_(torch.from_numpy(B).cuda())
+
+    for s in range(warmup):
+        for dt in DTYPES:
+            launch(dt, s % nslot)
+    torch.cuda.synchronize()
+    ev = {dt: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)] for dt in DTYPES}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(steps):
+        for dt in DTYPES:
+            ev[dt][s][0].record(stream)
+            launch(dt, (warmup + s) % nslot)
+            ev[dt][s][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    per = {}
+    for dt in DTYPES:
+        ms = [a.elapsed_time(b) for a, b in ev[dt]]
+        avg = float(np.mean(ms))
+        flops = lapack_flops(dt, m, n) * batch
+        nbytes = small_bytes(dt, m, n) * batch
+        per[dt] = {"ms_per_launch": avg, "gflops": flops / avg / 1e6,
+                   "hbm_gbs": nbytes / avg / 1e6, "hbm_frac": nbytes / avg / 1e6 / HBM_PEAK_GBS,
+                   "bytes_per_launch": nbytes, "rel_err": parity.get(dt)}
+    step_flops = sum(lapack_flops(dt, m, n) * batch for dt in DTYPES)
+    ms_per_step = total_ms / steps
+    return {"ms_per_step": ms_per_step, "gflops": step_flops / ms_per_step / 1e6, "per_dtype": per,
+            "wall_s": wall, "host": host}
+
+
+def bench_solve_tri(hs, torch, runs=2000):
+    """The SOLVE_TRI shape of the llama.cpp PR: A [64,64,4,2], B [6,64,4,2], f32."""
+    import oracle
+    import synth
+    n, k, e2, e3 = 64, 6, 4, 2
+    nb = e2 * e3
+    A = synth.tri("f32", n, nb, seed=SEED_CFG0, offdiag_div=64, layout="row")
+    B = synth.rhs("f32", n, k, nb, seed=SEED_CFG0 + 1, layout="row")
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    dX = torch.empty_like(dB)
+    stream = torch.cuda.current_stream()
+    args = (n, k, dA, dB, dX, e2, e3, n, n * n, e2 * n * n, k, n * k, e2 * n * k, k, n * k, e2 * n * k,
+            stream.cuda_stream)
+    assert hs.hsma_solve_tri_f32(*args) == hs.SUCCESS
+    torch.cuda.synchronize()
+    Xo = oracle.trsm(A, B)
+    X = dX.cpu().numpy()
+    err = float(np.sqrt(np.sum((X - Xo) ** 2) / np.sum(Xo ** 2)))
+    nmse = err ** 2
+    for _ in range(50):
+        hs.hsma_solve_tri_f32(*args)
+    samples = []
+    for rep in range(10):   # 10 samples, the first one a warm-up, mean of the last 9
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(runs // 10):
+            hs.hsma_solve_tri_f32(*args)
+        b.record(stream)
+        torch.cuda.synchronize()
+        samples.append(a.elapsed_time(b) * 1e3 / (runs // 10))
+    us = float(np.mean(samples[1:]))
+    nbytes = ggml_bytes(n, k, nb, 4)
+    return {"shape": "A[64,64,4,2] B[6,64,4,2] f32 (ggml layout, out of place)",
+            "us_per_call": us, "ggml_kB_per_run": nbytes / 1024, "ggml_GiB_per_s": nbytes / (us * 1e-6) / 2 ** 30,
+            "gflops": lapack_flops("f32", n, k) * nb / (us * 1e-6) / 1e9, "rel_err": err, "nmse": nmse,
+            "launches_timed": runs}
+
+
+def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0):
+    """One blocked solve per dtype at m = n, restored B between runs (untimed)."""
+    import synth
+    out = {}
+    stream = torch.cuda.current_stream()
+    for dt in dtypes:
+        log("blocked", dt, m)
+        A = synth.tri(dt, m, seed=SEED_CFG3)
+        B = synth.rhs(dt, m, m, seed=SEED_CFG3 + 1)
+        dA, dB0 = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dB = dB0.clone()
+        f = hs.entry("ex", dt)
+        opts = {"nb": nb, "path": hs.PATH_BLOCKED}
+        times = []
+        for r in range(runs + 1):     # first run is a warm-up
+            dB.copy_(dB0)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st = f(m, m, 1.0, dA, m, dB, m, opts, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if st != hs.SUCCESS:
+                raise hs.HsmaError(st, "trsm_ex_" + dt)
+            times.append(a.elapsed_time(b))
+        ms = float(np.mean(times[1:]))
+        # sampled parity: 64 seeded columns against the oracle
+        import oracle
+        cols = synth.pick_columns(m, 64, seed=SEED_CFG3)
+        Xg = dB[0, torch.from_numpy(cols).cuda()].cpu().numpy().T
+        Xo = oracle.trsm(A[0].T, B[0, cols].T)
+        err = float(np.linalg.norm(Xg.astype(Xo.dtype) - Xo) / np.linalg.norm(Xo))
+        # diagonal-inversion share: the inversion alone, same N_B
+        nbu = nb or hs.hsma_trsm_block_size(hs.DTYPE_CODE[dt], m)
+        nt = (m + nbu - 1) // nbu
+        inv = torch.empty(nt * nbu * nbu, dtype=dB.dtype, device="cuda")
+        dts = []
+        for r in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hs.entry("diag_inv", dt)(m, nbu, nbu // 8, dA, m, inv, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            dts.append(a.elapsed_time(b))
+        inv_ms = float(np.mean(dts[1:]))
+        flops = lapack_flops(dt, m, m)
+        out[dt] = {"ms": ms, "gflops": flops / ms / 1e6, "nb": nbu,
+                   "mfma_peak_frac": flops / ms / 1e9 / MFMA_PEAK_TFLOPS[dt],
+                   "diag_inv_ms": inv_ms, "diag_inv_share": inv_ms / ms, "rel_err_64cols": err}
+        del dA, dB0, dB, inv, A, B
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(host, m=64, n=64):
+    """The CPU oracle (as it stands) on the same step's problems, all host threads it is given."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    flops = 0
+    for dt in DTYPES:
+        A, B = host[dt]
+        oracle.trsm(A[:, :, :m].transpose(0, 2, 1), B[:, :, :m].transpose(0, 2, 1), threads=threads)
+        flops += lapack_flops(dt, m, n) * A.shape[0]
+    sec = time.perf_counter() - t0
+    return {"value": flops / sec / 1e9, "unit": "GFLOPS", "cores": threads, "kind": "oracle",
+            "sample": "the full step: 4096 problems x 4 dtypes (m=n=64), plain C double-precision "
+                      "forward substitution, %d threads on %s" % (threads, cpu_model()),
+            "seconds": sec}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batched", choices=["batched", "blocked"])
+    ap.add_argument("--m", type=int, default=8192, help="blocked workload size (m = n)")
+    ap.add_argument("--dtypes", default="f32,f64,c64,c128")
+    ap.add_argument("--nb", type=int, default=0, help="blocked N_B override (0: table)")
+    ap.add_argument("--no-blocked", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the work shards by "
+              "right-hand-side columns, see the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import triangular_solve_amd as hs
+    torch.cuda.set_device(0)
+
+    if args.workload == "blocked":
+        dts = args.dtypes.split(",")
+        res = bench_blocked(hs, torch, args.m, dts, runs=max(2, args.steps), nb=args.nb)
+        tot_flops = sum(lapack_flops(dt, args.m, args.m) for dt in dts)
+        tot_ms = sum(r["ms"] for r in res.values())
+        dom = max(res, key=lambda d: res[d]["ms"])
+        line = {"metric": METRIC, "value": tot_flops / tot_ms / 1e6, "unit": "GFLOPS", "n_gpus": 1,
+                "steps": max(2, args.steps), "warmup": 1, "ms_per_step": tot_ms, "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "+".join(dts), "data": "synthetic",
+                "config": {"workload": "blocked trsm m=n=%d, one solve per dtype (%s), column-major, "
+                                       "alpha=1, N_B from table" % (args.m, ",".join(dts)),
+                           "m": args.m, "n": args.m},
+                "roofline": {"bound": "mfma", "achieved": res[dom]["gflops"] / 1e3,
+                             "peak": MFMA_PEAK_TFLOPS[dom], "unit": "TFLOP/s",
+                             "frac": res[dom]["mfma_peak_frac"], "traffic": None,
+                             "kernel": "whole blocked solve, %s (LAPACK flop count)" % dom},
+                "blocked": res}
+        print(json.dumps(line), flush=True)
+        return
+
+    log("batched small regime")
+    bt = bench_batched(hs, torch, args.steps, args.warmup)
+    per = bt["per_dtype"]
+    dom = max(per, key=lambda d: per[d]["ms_per_launch"])
+    log("solve_tri shape")
+    st = bench_solve_tri(hs, torch)
+    blocked = None
+    if not args.no_blocked:
+        blocked = bench_blocked(hs, torch, 8192, DTYPES, runs=3)
+    cpu = None if args.no_cpu else cpu_baseline(bt["host"])
+    line = {
+        "metric": METRIC, "value": bt["gflops"], "unit": "GFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": bt["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32+f64+c64+c128", "data": "synthetic",
+        "config": {"workload": "batched trsm, 4096 column-major problems of m=n=64 per dtype, "
+                               "f32+f64+c64+c128 (one launch each), left/lower/no-trans/non-unit, alpha=1",
+                   "m": 64, "n": 64, "batch": 4096},
+        "roofline": {"bound": "hbm", "achieved": per[dom]["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": per[dom]["hbm_frac"], "traffic": None,
+                     "kernel": "colane_kernel (%s), %d algorithmic bytes per launch" % (dom, per[dom]["bytes_per_launch"])},
+        "cpu_baseline": cpu,
+        "per_dtype": per,
+        "solve_tri": st,
+        "blocked_8192": blocked,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
