@@ -163,6 +163,43 @@ hipError_t small_rowlane(const T *A, int64_t sai, int64_t saj, int64_t sa2, int6
 
 template <typename T>
 using cptr = const __attribute__((address_space(4))) T *;
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+
+// p, made to look modified once dep is available (no instruction emitted),
+// returned as a global-address-space pointer so loads through it stay
+// global_load (a generic pointer would turn them into flat loads, which also
+// count against the scalar-load counter).
+template <typename T, typename D>
+__device__ __forceinline__ gptr<T> global_after(T *p, const D &dep)
+{
+    uint64_t a = (uint64_t)p;
+    if constexpr (traits<D>::is_complex) asm volatile("" : "+v"(a) : "v"(dep.re));
+    else asm volatile("" : "+v"(a) : "v"(dep));
+    return (gptr<T>)a;
+}
+
+// Same for a wave-uniform pointer (kept in SGPRs).
+template <typename T, typename D>
+__device__ __forceinline__ T *uniform_after(T *p, const D &dep)
+{
+    uint64_t a = (uint64_t)p;
+    if constexpr (traits<D>::is_complex) asm volatile("" : "+s"(a) : "v"(dep.re));
+    else asm volatile("" : "+s"(a) : "v"(dep));
+    return (T *)a;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_global(gptr<T> p, int idx)
+{
+    if constexpr (traits<T>::is_complex) {
+        using R = typename traits<T>::real;
+        const gptr<R> q = (gptr<R>)p;
+        return T{q[2 * idx], q[2 * idx + 1]};
+    } else {
+        return p[idx];
+    }
+}
 
 // Wave-uniform read through the constant address space (scalar loads).
 template <typename T>
@@ -177,13 +214,6 @@ __device__ __forceinline__ T ld_uniform(cptr<T> p, int idx)
     }
 }
 
-// Number of coefficients read per scalar-load group: 16 dwords.
-template <typename T>
-constexpr int kGroup = (int)(64 / sizeof(T));
-
-// w[r] -= a(row0 + r, col) * x for r in [RLO, P): one column segment of A,
-// read as wave-uniform scalars in groups of kGroup so that the SGPR working
-// set stays bounded (a scheduling barrier separates the groups).
 // Empty asm that makes v look modified after `dep` is available: values
 // derived from v cannot be computed before dep. Emits no instruction.
 template <typename V, typename T>
@@ -193,30 +223,174 @@ __device__ __forceinline__ void order_after(V &v, const T &dep)
     else asm volatile("" : "+s"(v) : "v"(dep));
 }
 
-template <typename T, int P, int RLO>
-__device__ __forceinline__ void seg_update(T (&w)[P], cptr<T> acol, T x)
+// Compile-time plan of the coefficient stream of one row panel [R0, R0+P)
+// of the lane-per-column solve. The stream is a list of column segments:
+// first the R0 earlier columns (rows R0..R0+P-1 each, applied with the
+// finished x_k read back), then the panel's own columns j (rows below j).
+// Segments are cut into pieces and the pieces packed into batches of at
+// most G coefficients. A batch is fetched with scalar loads and consumed
+// after a single wait: scalar loads can return out of order, so every wait
+// is a full wait, and fewer, larger batches mean fewer exposed latencies.
+template <int P, int R0, int G>
+struct PanelPlan {
+    struct Piece {
+        int col, lo, hi;  // column of A, panel-local rows [lo, hi)
+        int first;        // first piece of its segment: x is formed here
+        int reload;       // segment of an earlier panel: x is read back
+    };
+    static constexpr int count()
+    {
+        int n = 0;
+        for (int k = 0; k < R0; ++k) n += (P + G - 1) / G;
+        for (int j = 0; j < P; ++j) n += (P - 1 - j) == 0 ? 1 : (P - 1 - j + G - 1) / G;
+        return n;
+    }
+    static constexpr int NP = count();
+    struct Table {
+        Piece pc[NP];
+        int off[NP];       // offset of the piece inside its batch buffer
+        int bfirst[NP + 1];
+        int nbatch;
+    };
+    static constexpr Table build()
+    {
+        Table t{};
+        int n = 0;
+        for (int k = 0; k < R0; ++k)
+            for (int lo = 0; lo < P; lo += G)
+                t.pc[n++] = Piece{k, lo, lo + G < P ? lo + G : P, lo == 0, 1};
+        for (int j = 0; j < P; ++j) {
+            if (j + 1 == P) { t.pc[n++] = Piece{R0 + j, P, P, 1, 0}; continue; }
+            for (int lo = j + 1; lo < P; lo += G)
+                t.pc[n++] = Piece{R0 + j, lo, lo + G < P ? lo + G : P, lo == j + 1, 0};
+        }
+        int b = 0, used = 0;
+        t.bfirst[0] = 0;
+        for (int i = 0; i < NP; ++i) {
+            const int L = t.pc[i].hi - t.pc[i].lo;
+            if (used + L > G && used > 0) { ++b; used = 0; t.bfirst[b] = i; }
+            t.off[i] = used;
+            used += L;
+        }
+        t.nbatch = b + 1;
+        t.bfirst[t.nbatch] = NP;
+        return t;
+    }
+    static constexpr Table T = build();
+};
+
+// Coefficients per batch: 64 dwords of SGPRs.
+template <typename T>
+constexpr int kBatch = (int)(256 / sizeof(T));
+
+// Per-panel state shared by the batch recursion below.
+template <typename T, int P>
+struct PanelState {
+    T w[P];       // this lane's rows of the panel
+    T x;          // multiplier of the current column segment
+    cptr<T> a4;   // A of this problem (scalar loads)
+    int64_t lda;
+    T *Bc;        // this lane's column of B (read back finished rows)
+    T myinv;      // 1/a_ll of this lane's row index l
+    T alpha_inv;
+};
+
+// Scalar loads of the pieces [Q, Q1) of a batch into cb.
+template <typename T, int P, int R0, int G, int Q, int Q1>
+__device__ __forceinline__ void batch_load(T (&cb)[G], cptr<T> ap, int64_t lda)
 {
-    constexpr int G = kGroup<T>;
-    static_for<RLO / G, (P + G - 1) / G>([&](auto gi) {
-        constexpr int g0 = decltype(gi)::value * G;
-        constexpr int lo = g0 > RLO ? g0 : RLO;
-        constexpr int hi = g0 + G < P ? g0 + G : P;
-        // issue this group's scalar loads only once x exists
-        cptr<T> ap = acol;
-        order_after(ap, x);
-        T a[hi - lo];
-        static_for<lo, hi>([&](auto r) { a[r - lo] = ld_uniform<T>(ap, r); });
-        static_for<lo, hi>([&](auto r) { w[r] = fms(w[r], a[r - lo], x); });
+    if constexpr (Q < Q1) {
+        using Plan = PanelPlan<P, R0, G>;
+        constexpr auto pc = Plan::T.pc[Q];
+        constexpr int off = Plan::T.off[Q];
+        const cptr<T> colp = ap + (R0 + (int64_t)pc.col * lda);
+#pragma unroll
+        for (int r = pc.lo; r < pc.hi; ++r) cb[off + r - pc.lo] = ld_uniform<T>(colp, r);
+        batch_load<T, P, R0, G, Q + 1, Q1>(cb, ap, lda);
+    }
+}
+
+// The updates of pieces [Q, Q1) of a batch.
+template <typename T, int P, int R0, int G, int Q, int Q1>
+__device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb)[G])
+{
+    if constexpr (Q < Q1) {
+        using Plan = PanelPlan<P, R0, G>;
+        constexpr auto pc = Plan::T.pc[Q];
+        constexpr int off = Plan::T.off[Q];
+        if constexpr (pc.first) {
+            if constexpr (pc.reload) {
+                // finished x_k of an earlier panel, read back from B
+                const gptr<T> bk = global_after(st.Bc + pc.col, st.x);
+                st.x = mul(ld_global<T>(bk, 0), st.alpha_inv);
+            } else {
+                constexpr int j = pc.col - R0;
+                // Tie the broadcast of 1/a_jj to w[j] so the compiler cannot
+                // hoist all broadcasts to the top (that would exhaust SGPRs).
+                T inv = st.myinv;
+                if constexpr (traits<T>::is_complex) {
+                    asm volatile("" : "+v"(inv.re), "+v"(inv.im) : "v"(st.w[j].re), "v"(st.w[j].im));
+                } else {
+                    asm volatile("" : "+v"(inv) : "v"(st.w[j]));
+                }
+                st.x = mul(st.w[j], readlane(inv, pc.col));
+                st.w[j] = st.x;
+            }
+        }
+#pragma unroll
+        for (int r = pc.lo; r < pc.hi; ++r) st.w[r] = fms(st.w[r], cb[off + r - pc.lo], st.x);
+        batch_compute<T, P, R0, G, Q + 1, Q1>(st, cb);
+    }
+}
+
+// Batches [Bi, nbatch) of the panel at rows R0: fetch, one wait, update.
+template <typename T, int P, int R0, int G, int Bi>
+__device__ __forceinline__ void run_batches(PanelState<T, P> &st)
+{
+    using Plan = PanelPlan<P, R0, G>;
+    if constexpr (Bi < Plan::T.nbatch) {
+        constexpr int p0 = Plan::T.bfirst[Bi], p1 = Plan::T.bfirst[Bi + 1];
+        // fetch this batch once the previous one has been consumed
+        cptr<T> ap = st.a4;
+        order_after(ap, st.x);
+        T cb[G];
+        batch_load<T, P, R0, G, p0, p1>(cb, ap, st.lda);
+        batch_compute<T, P, R0, G, p0, p1>(st, cb);
         __builtin_amdgcn_sched_barrier(0);
-    });
+        run_batches<T, P, R0, G, Bi + 1>(st);
+    }
+}
+
+template <typename T, int P, int NPANEL, int PI>
+__device__ __forceinline__ void run_panels(PanelState<T, P> &st, bool live, T alpha,
+                                           typename traits<T>::real wlast)
+{
+    if constexpr (PI < NPANEL) {
+        constexpr int r0 = PI * P;
+        // a later panel's rows are loaded only after the earlier panel is done
+        const gptr<T> bp = global_after(st.Bc, wlast);
+#pragma unroll
+        for (int r = 0; r < P; ++r) st.w[r] = ld_global<T>(bp, r0 + r);
+        st.x = zero_of(T());
+        run_batches<T, P, r0, kBatch<T>, 0>(st);
+        // The solve ran on B itself; alpha is applied to X on the way out
+        // (A (alpha^{-1} X) = B has the same substitution with alpha factored out).
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < P; ++r) st.Bc[r0 + r] = mul(alpha, st.w[r]);
+        }
+        typename traits<T>::real wl;
+        if constexpr (traits<T>::is_complex) wl = st.w[P - 1].re; else wl = st.w[P - 1];
+        run_panels<T, P, NPANEL, PI + 1>(st, live, alpha, wl);
+    }
 }
 
 template <typename T, int NPANEL>
-__global__ void __launch_bounds__(256) colane_kernel(const T *__restrict__ A, int64_t lda,
-                                                      int64_t strideA, T *__restrict__ B,
-                                                      int64_t ldb, int64_t strideB, int64_t n,
-                                                      int64_t nchunks, int64_t items, T alpha,
-                                                      T alpha_inv)
+__global__ void __launch_bounds__(256, 4) colane_kernel(const T *__restrict__ A, int64_t lda,
+                                                         int64_t strideA, T *__restrict__ B,
+                                                         int64_t ldb, int64_t strideB, int64_t n,
+                                                         int64_t nchunks, int64_t items, T alpha,
+                                                         T alpha_inv)
 {
     constexpr int M = 64;
     constexpr int P = M / NPANEL;
@@ -232,47 +406,50 @@ __global__ void __launch_bounds__(256) colane_kernel(const T *__restrict__ A, in
     const bool live = c < n;
 
     const T *Ap = A + prob * strideA;
-    const cptr<T> a4 = (cptr<T>)Ap;
     // Lanes past n work on a copy of the wave's first column (always valid)
     // and never store, so loads need no guard.
-    T *Bc = B + prob * strideB + (live ? c : cfirst) * ldb;
+    T *Bc0 = B + prob * strideB + cfirst * ldb;
 
-    // 1/a_ll for this lane's row index l; step j broadcasts lane j's value.
-    const T myinv = recip(Ap[lane + lane * lda]);
+    PanelState<T, P> st;
+    st.a4 = (cptr<T>)Ap;
+    st.lda = lda;
+    st.Bc = Bc0 + (live ? lane : 0) * ldb;
+    st.alpha_inv = alpha_inv;
 
-    static_for<0, NPANEL>([&](auto pi) {
-        constexpr int r0 = decltype(pi)::value * P;
-        // The solve runs on B itself; alpha is applied to X on the way out
-        // (A (alpha^{-1} X) = B has the same substitution with alpha factored out).
-        T w[P];
-        static_for<0, P>([&](auto r) { w[r] = Bc[r0 + r]; });
+    // Warm L2 with this problem's triangle: lane l touches every cache line
+    // of column l from the diagonal down, one dword per line, so the scalar
+    // loads below find the coefficients in L2 instead of HBM.
+    constexpr int kLine = 128 / (int)sizeof(T);  // elements per 128-byte line
+    constexpr int kTouch = 64 / kLine + 2;
+    uint32_t touch[kTouch];
+    {
+        const uint32_t *colp = (const uint32_t *)(Ap + lane * lda);
+#pragma unroll
+        for (int q = 0; q < kTouch; ++q) {
+            int row = lane + q * kLine;
+            row = row < 63 ? row : 63;
+            touch[q] = colp[row * (int)(sizeof(T) / 4)];
+        }
+    }
+    st.myinv = recip(Ap[lane + lane * lda]);
+    run_panels<T, P, NPANEL, 0>(st, live, alpha, typename traits<T>::real(0));
+#pragma unroll
+    for (int q = 0; q < kTouch; ++q) asm volatile("" ::"v"(touch[q]));
+}
 
-        // Contributions of the finished rows above this panel.
-        static_for<0, r0>([&](auto k) {
-            // reload the finished x_k only after the previous update is issued
-            T *bk = Bc + k;
-            if constexpr (traits<T>::is_complex) asm volatile("" : "+v"(bk) : "v"(w[P - 1].re));
-            else asm volatile("" : "+v"(bk) : "v"(w[P - 1]));
-            const T x = mul(*bk, alpha_inv);
-            seg_update<T, P, 0>(w, a4 + (r0 + k * lda), x);
-        });
-        // Substitution inside the panel.
-        static_for<0, P>([&](auto jj) {
-            constexpr int j = decltype(jj)::value;
-            // Tie the broadcast of 1/a_jj to w[j] so the compiler cannot hoist
-            // all 64 broadcasts to the top (that would exhaust the SGPRs).
-            T inv = myinv;
-            if constexpr (traits<T>::is_complex) {
-                asm volatile("" : "+v"(inv.re), "+v"(inv.im) : "v"(w[j].re), "v"(w[j].im));
-            } else {
-                asm volatile("" : "+v"(inv) : "v"(w[j]));
-            }
-            const T x = mul(w[j], readlane(inv, r0 + j));
-            w[j] = x;
-            if constexpr (j + 1 < P) seg_update<T, P, j + 1>(w, a4 + (r0 + (int64_t)(r0 + j) * lda), x);
-        });
-        if (live) static_for<0, P>([&](auto r) { Bc[r0 + r] = mul(alpha, w[r]); });
-    });
+// Compute units of the current device (cached per device).
+static int num_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
 }
 
 template <typename T>
@@ -283,10 +460,19 @@ hipError_t small_colane(int64_t n, T alpha, const T *A, int64_t lda, int64_t str
     const int64_t items = nchunks * batch;
     const int64_t blocks = (items + 3) / 4;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    constexpr int NP = sizeof(T) == 16 ? 2 : 1;
+    // Row panels keep the register-resident part of a column at 64 VGPRs or
+    // less (<= 128 VGPRs in all), i.e. at least 4 waves per SIMD: 4096
+    // problems then run as one round of 16 waves per CU.
+    constexpr int NP = (int)sizeof(T) / 4;
     // Earlier panels' rows are read back from B already scaled by alpha.
     const T alpha_inv = host_recip(alpha);
-    hipLaunchKernelGGL((colane_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), 0, s, A, lda,
+    // Spread the workgroups evenly over the CUs: left alone, the dispatcher
+    // may pack up to the occupancy limit onto fewer CUs. Reserving LDS (the
+    // kernel uses none) caps the workgroups per CU at the even share.
+    const int64_t per_cu = (blocks + num_cus() - 1) / num_cus();
+    size_t lds = 0;
+    if (per_cu >= 3 && per_cu < 8) lds = ((size_t)(160 * 1024) / (size_t)per_cu) & ~(size_t)1023;
+    hipLaunchKernelGGL((colane_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), lds, s, A, lda,
                        strideA, B, ldb, strideB, n, nchunks, items, alpha, alpha_inv);
     return hipGetLastError();
 }
