@@ -168,17 +168,32 @@ hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *in
 
 // ---------------------------------------------------------------------------
 // Matrix-core GEMM
+//
+// C = beta*C + alpha*A*B. A 256-thread workgroup owns a 128 x 128 tile of C
+// (four waves, 64 x 64 each). K advances in steps of BK through two LDS
+// buffers: the next step's tiles are fetched from HBM into registers while
+// the matrix cores work on the current one, then written to the other
+// buffer; one barrier per step. Global loads are 16 bytes wide along the
+// contiguous dimension of each column-major operand.
+//
+// Operand roles: the MFMA "row" operand runs over output columns j (from the
+// B tile) and the MFMA "column" operand over output rows i (from the A tile),
+// so consecutive lanes own consecutive rows of the column-major C and C
+// traffic coalesces. Inside a step the k index is permuted: lane group h
+// handles k = KS*h + s at MFMA sub-step s, so each lane's B fragment for KS
+// sub-steps is one contiguous 16-byte LDS read (the same permutation is used
+// for A, so every k is still summed exactly once).
 
 template <typename R> struct mfma_cfg;
 // FP32: v_mfma_f32_32x32x2f32, a wave owns 64 x 64 outputs as 2 x 2 blocks.
 template <> struct mfma_cfg<float> {
-    static constexpr int BLK = 32, KSTEP = 2, NB = 2;
+    static constexpr int BLK = 32, LG = 2, NB = 2, BK = 32;  // LG: lane groups along k
     using acc_t = f32x16;
     static constexpr int NACC = 16;
 };
 // FP64: v_mfma_f64_16x16x4f64, a wave owns 64 x 64 outputs as 4 x 4 blocks.
 template <> struct mfma_cfg<double> {
-    static constexpr int BLK = 16, KSTEP = 4, NB = 4;
+    static constexpr int BLK = 16, LG = 4, NB = 4, BK = 16;
     using acc_t = f64x4;
     static constexpr int NACC = 4;
 };
@@ -192,9 +207,13 @@ __device__ inline f64x4 mfma_op(double a, double b, f64x4 c)
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
-constexpr int kBM = 128, kBN = 128, kBK = 16;
-constexpr int kPadA = 4;  // As[k][i] row padding (elements)
-constexpr int kPadB = 1;  // Bs[j][k] row padding (elements)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+template <typename R> struct vec16;
+template <> struct vec16<float> { using type = f32x4; static constexpr int N = 4; };
+template <> struct vec16<double> { using type = f64x2; static constexpr int N = 2; };
+
+constexpr int kBM = 128, kBN = 128;
 
 // Real view of the product: Mr x N output from an Mr x Kr "A" and a Kr x N
 // "B". For complex T, Mr = 2M, Kr = 2K, and B, C are the complex arrays read
@@ -209,24 +228,25 @@ struct GemmArgs {
     R *C;
     int64_t ldc;  // real units
     int64_t Mr, N, Kr;
-    R alpha, beta;
+    R alpha, cscale;  // C = alpha * (cscale * C + A*B); cscale = beta / alpha, alpha != 0
     int a_lower;
 };
 
-// The MFMA "row" operand runs over output columns j (from Bs) and the MFMA
-// "column" operand over output rows i (from As). That makes consecutive lanes
-// touch consecutive rows of the column-major C, so C reads and writes
-// coalesce.
-template <typename T>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> p)
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 {
     using R = typename traits<T>::real;
     using cfg = mfma_cfg<R>;
+    using V16 = typename vec16<R>::type;
+    constexpr int VN = vec16<R>::N;           // reals per 16 bytes
     constexpr bool CPX = traits<T>::is_complex;
-    constexpr int BLK = cfg::BLK, KS = cfg::KSTEP, NBK = cfg::NB;
-    constexpr int LDA_S = kBM + kPadA, LDB_S = kBK + kPadB;
-    __shared__ R As[kBK * LDA_S];
-    __shared__ R Bs[kBN * LDB_S];
+    constexpr int BLK = cfg::BLK, LG = cfg::LG, NBK = cfg::NB, BK = cfg::BK;
+    constexpr int KS = BK / LG / (BK / (LG * VN)) ;  // k per lane group per 16-byte read = VN
+    static_assert(KS == VN, "one 16-byte B read per lane group");
+    constexpr int LDA_S = kBM + 4 / (int)(sizeof(R) / 4);   // As[k][i] row stride (+16 bytes)
+    constexpr int LDB_S = BK + VN;                           // Bs[j][k] row stride (+16 bytes)
+    __shared__ __attribute__((aligned(16))) R As[2][BK * LDA_S];
+    __shared__ __attribute__((aligned(16))) R Bs[2][kBN * LDB_S];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -239,90 +259,149 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> p)
     int64_t kend = p.Kr;
     if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
 
-    // ---- global -> register staging of one K tile ----
-    constexpr int A_PER = CPX ? (kBM / 2) * (kBK / 2) / 256 : kBM * kBK / 256;
-    constexpr int B_PER = kBK * kBN / 256;
-    T ra[A_PER];
-    R rbv[B_PER];
+    // ---- staging of one K step: A as 16-byte chunks along i, B along k ----
+    // A tile: BK x kBM reals = (kBM/VN) chunks per k row; chunks per thread:
+    constexpr int A_CH = BK * kBM / VN / 256;
+    constexpr int B_CH = BK * kBN / VN / 256;
+    // PF K steps of staging registers: step s+PF is fetched while step s is
+    // multiplied (with PF = 2, s+1 already sits in the other LDS buffer).
+    // Measured on MI355X, PF = 2 gained nothing over PF = 1, which needs
+    // fewer registers.
+    constexpr int PF = 1;
+    V16 ra[PF][A_CH], rb[PF][B_CH];
 
-    auto load_tile = [&](int64_t k0) {
+    auto load_step = [&](int64_t k0, int slot) {
 #pragma unroll
-        for (int e = 0; e < A_PER; ++e) {
+        for (int e = 0; e < A_CH; ++e) {
             const int idx = tid + 256 * e;
+            const int ic = idx % (kBM / VN), kl = idx / (kBM / VN);  // chunk column, k row
+            const int64_t k = k0 + kl;
+            V16 v;
             if constexpr (CPX) {
-                const int il = idx % (kBM / 2), kl = idx / (kBM / 2);
-                const int64_t ic = i0 / 2 + il, kc = k0 / 2 + kl;
-                const bool ok = ic < p.Mr / 2 && kc < p.Kr / 2 && (!p.a_lower || kc <= ic);
-                ra[e] = ok ? p.A[ic + kc * p.lda] : zero_of(T());
+                // VN reals of one real row = VN/2 complex entries of A's complex row ...
+                // real row index r = 2*ic_c + p  -> complex rows i0/2 + ic*VN/2 ...
+                // Load the complex entries (kc = k/2 column, rows ic*VN/2 .. +VN/2); the
+                // expansion to [[re, -im], [im, re]] happens when writing LDS.
+                const int64_t kc = k >> 1;
+                const int64_t ib = i0 / 2 + (int64_t)ic * (VN / 2);
+                R tmp[VN];
+#pragma unroll
+                for (int t = 0; t < VN / 2; ++t) {
+                    const int64_t irow = ib + t;
+                    const bool ok = irow < p.Mr / 2 && kc < p.Kr / 2 && (!p.a_lower || kc <= irow);
+                    T a = ok ? p.A[irow + kc * p.lda] : zero_of(T());
+                    // row 2kc (k even): (re, im); row 2kc+1 (k odd): (-im, re)
+                    if ((k & 1) == 0) { tmp[2 * t] = a.re; tmp[2 * t + 1] = a.im; }
+                    else { tmp[2 * t] = -a.im; tmp[2 * t + 1] = a.re; }
+                }
+#pragma unroll
+                for (int t = 0; t < VN; ++t) v[t] = tmp[t];
             } else {
-                const int il = idx % kBM, kl = idx / kBM;
-                const int64_t i = i0 + il, k = k0 + kl;
-                const bool ok = i < p.Mr && k < p.Kr && (!p.a_lower || k <= i);
-                ra[e] = ok ? p.A[i + k * p.lda] : R(0);
+                const int64_t ib = i0 + (int64_t)ic * VN;
+                const bool full = VEC && ib + VN <= p.Mr && k < p.Kr && (!p.a_lower || k <= ib);
+                if (full) {
+                    v = *(const V16 *)(p.A + ib + k * p.lda);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < VN; ++t) {
+                        const int64_t i = ib + t;
+                        const bool ok = i < p.Mr && k < p.Kr && (!p.a_lower || k <= i);
+                        v[t] = ok ? p.A[i + k * p.lda] : R(0);
+                    }
+                }
             }
+            ra[slot][e] = v;
         }
 #pragma unroll
-        for (int e = 0; e < B_PER; ++e) {
+        for (int e = 0; e < B_CH; ++e) {
             const int idx = tid + 256 * e;
-            const int kl = idx % kBK, jl = idx / kBK;
-            const int64_t k = k0 + kl, j = j0 + jl;
-            rbv[e] = (k < p.Kr && j < p.N) ? p.B[k + j * p.ldb] : R(0);
+            const int kc = idx % (BK / VN), jl = idx / (BK / VN);
+            const int64_t kb = k0 + kc * VN, j = j0 + jl;
+            V16 v;
+            if (VEC && kb + VN <= p.Kr && j < p.N) {
+                v = *(const V16 *)(p.B + kb + j * p.ldb);
+            } else {
+#pragma unroll
+                for (int t = 0; t < VN; ++t) v[t] = (kb + t < p.Kr && j < p.N) ? p.B[kb + t + j * p.ldb] : R(0);
+            }
+            rb[slot][e] = v;
         }
     };
-    auto store_tile = [&]() {
+    auto store_step = [&](int buf, int slot) {
 #pragma unroll
-        for (int e = 0; e < A_PER; ++e) {
+        for (int e = 0; e < A_CH; ++e) {
             const int idx = tid + 256 * e;
-            if constexpr (CPX) {
-                const int il = idx % (kBM / 2), kl = idx / (kBM / 2);
-                const T a = ra[e];
-                // real 2 x 2 block of a complex entry: [[re, -im], [im, re]]
-                As[(2 * kl) * LDA_S + 2 * il] = a.re;
-                As[(2 * kl) * LDA_S + 2 * il + 1] = a.im;
-                As[(2 * kl + 1) * LDA_S + 2 * il] = -a.im;
-                As[(2 * kl + 1) * LDA_S + 2 * il + 1] = a.re;
-            } else {
-                const int il = idx % kBM, kl = idx / kBM;
-                As[kl * LDA_S + il] = ra[e];
-            }
+            const int ic = idx % (kBM / VN), kl = idx / (kBM / VN);
+            *(V16 *)&As[buf][kl * LDA_S + ic * VN] = ra[slot][e];
         }
 #pragma unroll
-        for (int e = 0; e < B_PER; ++e) {
+        for (int e = 0; e < B_CH; ++e) {
             const int idx = tid + 256 * e;
-            const int kl = idx % kBK, jl = idx / kBK;
-            Bs[jl * LDB_S + kl] = rbv[e];
+            const int kc = idx % (BK / VN), jl = idx / (BK / VN);
+            *(V16 *)&Bs[buf][jl * LDB_S + kc * VN] = rb[slot][e];
         }
+    };
+
+    const int lrow = lane % BLK;  // MFMA operand row / output column inside a block
+    const int lg = lane / BLK;    // lane group along k
+
+    // Output-row index of accumulator register r (lane layouts of the two MFMA forms).
+    auto jrow = [&](int r) -> int {
+        if constexpr (BLK == 32) return 8 * (r / 4) + 4 * lg + (r % 4);
+        else return lg + 4 * r;
     };
 
     typename cfg::acc_t acc[NBK][NBK];
 #pragma unroll
-    for (int a = 0; a < NBK; ++a)
+    for (int b = 0; b < NBK; ++b)
 #pragma unroll
-        for (int b = 0; b < NBK; ++b)
+        for (int a = 0; a < NBK; ++a)
 #pragma unroll
-            for (int r = 0; r < cfg::NACC; ++r) acc[a][b][r] = 0;
+            for (int r = 0; r < cfg::NACC; ++r) acc[b][a][r] = 0;
 
-    const int lrow = lane % BLK;   // MFMA operand row / output column inside a block
-    const int lk = lane / BLK;     // MFMA k sub-index
-
-    if (kend > 0) load_tile(0);
-    for (int64_t k0 = 0; k0 < kend; k0 += kBK) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (k0 + kBK < kend) load_tile(k0 + kBK);
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += KS) {
-            R bj[NBK], ai[NBK];
-#pragma unroll
-            for (int b = 0; b < NBK; ++b) bj[b] = Bs[(wj + b * BLK + lrow) * LDB_S + kk + lk];
-#pragma unroll
-            for (int a = 0; a < NBK; ++a) ai[a] = As[(kk + lk) * LDA_S + wi + a * BLK + lrow];
+    const int nsteps = (int)((kend + BK - 1) / BK);
+    if (nsteps > 0) {
+        load_step(0, 0);
+        if (PF == 2 && nsteps > 1) load_step(BK, PF - 1);
+        store_step(0, 0);
+    }
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        const int buf = st & 1;
+        // PF = 2: slot (st+1)&1 holds step st+1 and slot st&1 is free for st+2
+        if (st + PF < nsteps) load_step((int64_t)(st + PF) * BK, PF == 2 ? (st & 1) : 0);
+        const R *as = As[buf];
+        const R *bs = Bs[buf];
+        // BK = NQ groups of LG*VN k values. The fragments of group q+1 are read
+        // from LDS before the MFMAs of group q are issued, so LDS latency
+        // overlaps matrix-core work.
+        constexpr int NQ = BK / (LG * VN);
+        V16 bv[2][NBK];
+        R av[2][VN][NBK];
+        auto read_frag = [&](int q, int slot) {
+            const int kq = q * LG * VN + lg * VN;  // this lane group's first k in the group
 #pragma unroll
             for (int b = 0; b < NBK; ++b)
+                bv[slot][b] = *(const V16 *)&bs[(wj + b * BLK + lrow) * LDB_S + kq];
 #pragma unroll
-                for (int a = 0; a < NBK; ++a) acc[b][a] = mfma_op(bj[b], ai[a], acc[b][a]);
+            for (int s = 0; s < VN; ++s)
+#pragma unroll
+                for (int a = 0; a < NBK; ++a) av[slot][s][a] = as[(kq + s) * LDA_S + wi + a * BLK + lrow];
+        };
+        read_frag(0, 0);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if (q + 1 < NQ) read_frag(q + 1, (q + 1) & 1);
+#pragma unroll
+            for (int s = 0; s < VN; ++s)
+#pragma unroll
+                for (int b = 0; b < NBK; ++b)
+#pragma unroll
+                    for (int a = 0; a < NBK; ++a)
+                        acc[b][a] = mfma_op(bv[q & 1][b][s], av[q & 1][s][a], acc[b][a]);
         }
+        if (st + 1 < nsteps) store_step(buf ^ 1, PF == 2 ? ((st + 1) & 1) : 0);
+        __syncthreads();
     }
 
     // ---- epilogue: acc[b][a] holds D[j][i] for j in block b, i in block a ----
@@ -332,17 +411,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs<T> p)
         for (int a = 0; a < NBK; ++a)
 #pragma unroll
             for (int r = 0; r < cfg::NACC; ++r) {
-                int jr;
-                // output-row index of register r (lane layouts of the two MFMA forms)
-                if constexpr (BLK == 32) jr = 8 * (r / 4) + 4 * lk + (r % 4);
-                else jr = lk + 4 * r;
                 const int64_t i = i0 + wi + a * BLK + lrow;
-                const int64_t j = j0 + wj + b * BLK + jr;
+                const int64_t j = j0 + wj + b * BLK + jrow(r);
                 if (i < p.Mr && j < p.N) {
-                    R v = p.alpha * acc[b][a][r];
                     R *cp = p.C + i + j * p.ldc;
-                    if (p.beta != R(0)) v += *cp;
-                    *cp = v;
+                    R v = acc[b][a][r];
+                    if (p.cscale != R(0)) v += p.cscale * *cp;
+                    *cp = p.alpha * v;
                 }
             }
 }
@@ -364,12 +439,27 @@ hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
     p.Mr = M * f;
     p.N = N;
     p.Kr = K * f;
-    p.alpha = alpha;
-    p.beta = beta;
     p.a_lower = a_lower ? 1 : 0;
+    if (alpha == R(0)) {
+        // C = beta * C with beta in {0, 1}: nothing to multiply
+        if (beta != R(0)) return hipSuccess;
+        p.alpha = R(1);
+        p.cscale = R(0);
+        K = 0;
+        p.Kr = 0;
+    } else {
+        p.alpha = alpha;
+        p.cscale = beta / alpha;
+    }
     const int64_t gx = (p.Mr + kBM - 1) / kBM, gy = (N + kBN - 1) / kBN;
     if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gemm_kernel<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
+    // 16-byte loads need 16-byte aligned columns of A (real types) and B.
+    const bool vec = (uintptr_t)A % 16 == 0 && (uintptr_t)B % 16 == 0 &&
+                     (lda * (int64_t)sizeof(T)) % 16 == 0 && (ldb * (int64_t)sizeof(T)) % 16 == 0;
+    if (vec)
+        hipLaunchKernelGGL((gemm_kernel<T, true>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<T, false>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
