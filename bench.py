@@ -239,6 +239,38 @@ def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0):
     return out
 
 
+def counter_workload(hs, torch):
+    """Three batched solves per dtype (4096 problems, m = n = 64), then a 1 GiB
+    device-to-device copy whose byte counts calibrate the HBM counters."""
+    for dt in DTYPES:
+        A, B = batched_inputs(dt, 64, 64, 4096, SEED_CFG1)
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        f = hs.entry("strided_batched", dt)
+        for _ in range(3):
+            hs.check(f(64, 64, 1.0, dA, 64, 4096, dB, 64, 4096, 4096), "strided_batched_" + dt)
+        torch.cuda.synchronize()
+        del dA, dB
+    x = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    log("counter workload done")
+
+
+# HBM bytes per launch of the batched small kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (profiles/colane_batched64_hbm_traffic.md), valid only for the
+# kernel source they were taken on: keyed by the SHA-256 of small.hip.
+MEASURED_TRAFFIC = {}
+
+
+def measured_traffic(dtype):
+    import hashlib
+    src = os.path.join(ROOT, "triangular_solve_amd", "csrc", "small.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    entry = MEASURED_TRAFFIC.get(h, {}).get(dtype)
+    return entry
+
+
 def cpu_baseline(host, m=64, n=64):
     """The CPU oracle (as it stands) on the same step's problems, all host threads it is given."""
     import oracle
@@ -261,7 +293,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="batched", choices=["batched", "blocked"])
+    ap.add_argument("--workload", default="batched", choices=["batched", "blocked", "counters"],
+                    help="counters: only three batched solves per dtype and a 1 GiB copy, for "
+                         "rocprofv3 --pmc runs")
     ap.add_argument("--m", type=int, default=8192, help="blocked workload size (m = n)")
     ap.add_argument("--dtypes", default="f32,f64,c64,c128")
     ap.add_argument("--nb", type=int, default=0, help="blocked N_B override (0: table)")
@@ -280,6 +314,9 @@ def main():
     import triangular_solve_amd as hs
     torch.cuda.set_device(0)
 
+    if args.workload == "counters":
+        counter_workload(hs, torch)
+        return
     if args.workload == "blocked":
         dts = args.dtypes.split(",")
         res = bench_blocked(hs, torch, args.m, dts, runs=max(2, args.steps), nb=args.nb)
@@ -318,7 +355,7 @@ def main():
                                "f32+f64+c64+c128 (one launch each), left/lower/no-trans/non-unit, alpha=1",
                    "m": 64, "n": 64, "batch": 4096},
         "roofline": {"bound": "hbm", "achieved": per[dom]["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": per[dom]["hbm_frac"], "traffic": None,
+                     "frac": per[dom]["hbm_frac"], "traffic": measured_traffic(dom),
                      "kernel": "colane_kernel (%s), %d algorithmic bytes per launch" % (dom, per[dom]["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "per_dtype": per,

@@ -55,7 +55,6 @@ template <typename T, int KW>
 __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
 {
     __shared__ T AT[64 * kLdsStride];
-    __shared__ T sinv[64];
 
     const int64_t b = blockIdx.x;
     const int64_t i2 = b % p.ne02, i3 = b / p.ne02;
@@ -63,35 +62,33 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
     const T *Bb = p.B + i2 * p.sb2 + i3 * p.sb3;
     T *Xb = p.X + i2 * p.sx2 + i3 * p.sx3;
     const int m = p.m;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int nthr = blockDim.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
 
-    if (tid < 64) {
-        T one = zero_of(T());
-        if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
-        const T d = tid < m ? Ab[tid * (p.sai + p.saj)] : one;
-        sinv[tid] = recip(d);
-    }
-    __syncthreads();
+    T one = zero_of(T());
+    if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
+    // Lane i owns row i: its own 1/a_ii, no exchange needed.
+    const T inv = recip(lane < m ? Ab[lane * (p.sai + p.saj)] : one);
 
     // Stage tril(A) scaled by its row's inverse diagonal, strictly lower part
     // only (diagonal and above are zero), transposed: AT[j][i] = a_ij / a_ii.
-    // The walk order follows the storage so global reads coalesce.
-    const bool colmajor = p.sai == 1;
-    for (int idx = tid; idx < 64 * 64; idx += nthr) {
-        const int i = colmajor ? (idx & 63) : (idx >> 6);
-        const int j = colmajor ? (idx >> 6) : (idx & 63);
-        T v = zero_of(T());
-        if (i < m && j < i) v = mul(Ab[i * p.sai + j * p.saj], sinv[i]);
-        AT[j * kLdsStride + i] = v;
+    // Wave w takes columns j = w, w + nw, ...; the loop is unrolled so the
+    // loads of a group are all in flight together.
+    const int per = (64 + nw - 1) / nw;
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        const int j = wave * per + t;
+        if (t < per && j < 64) {
+            T v = zero_of(T());
+            if (lane < m && j < lane) v = mul(Ab[lane * p.sai + j * p.saj], inv);
+            AT[j * kLdsStride + lane] = v;
+        }
     }
 
     // This wave's right-hand-side columns, one row per lane, pre-scaled the
     // same way: w_i = alpha * b_i / a_ii.
-    const int c0 = (blockIdx.y * (nthr >> 6) + wave) * KW;
-    const T inv = sinv[lane];
+    const int c0 = (blockIdx.y * nw + wave) * KW;
     T w[KW];
 #pragma unroll
     for (int q = 0; q < KW; ++q) {
@@ -104,13 +101,19 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
     // Forward substitution. After step j-1, lane j holds the finished x_j;
     // every lane below subtracts its (scaled) a_ij * x_j. Lanes at or above
     // j read a zero coefficient and keep their value.
-    for (int j = 0; j < m; ++j) {
+    auto step = [&](int j) {
         const T a = AT[j * kLdsStride + lane];
 #pragma unroll
         for (int q = 0; q < KW; ++q) {
             const T x = readlane(w[q], j);
             w[q] = fms(w[q], a, x);
         }
+    };
+    if (m == 64) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) step(j);
+    } else {
+        for (int j = 0; j < m; ++j) step(j);
     }
 
 #pragma unroll
@@ -386,7 +389,7 @@ __device__ __forceinline__ void run_panels(PanelState<T, P> &st, bool live, T al
 }
 
 template <typename T, int NPANEL>
-__global__ void __launch_bounds__(256, 4) colane_kernel(const T *__restrict__ A, int64_t lda,
+__global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(const T *__restrict__ A, int64_t lda,
                                                          int64_t strideA, T *__restrict__ B,
                                                          int64_t ldb, int64_t strideB, int64_t n,
                                                          int64_t nchunks, int64_t items, T alpha,
@@ -460,10 +463,13 @@ hipError_t small_colane(int64_t n, T alpha, const T *A, int64_t lda, int64_t str
     const int64_t items = nchunks * batch;
     const int64_t blocks = (items + 3) / 4;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    // Row panels keep the register-resident part of a column at 64 VGPRs or
-    // less (<= 128 VGPRs in all), i.e. at least 4 waves per SIMD: 4096
-    // problems then run as one round of 16 waves per CU.
-    constexpr int NP = (int)sizeof(T) / 4;
+    // Whole 64-row columns in registers for f32, f64 and c64 (no re-reads of
+    // finished rows); two row panels for c128, whose full column would take
+    // all 256 VGPRs. Measured on MI355X against 2/2/4 panels at 4 waves per
+    // SIMD: f64 139 -> 114 us, c64 149 -> 136 us, c128 422 -> 291 us per
+    // 4096 problems (re-read rows had been evicted from L2 and came back
+    // from HBM).
+    constexpr int NP = sizeof(T) == 16 ? 2 : 1;
     // Earlier panels' rows are read back from B already scaled by alpha.
     const T alpha_inv = host_recip(alpha);
     // Spread the workgroups evenly over the CUs: left alone, the dispatcher
