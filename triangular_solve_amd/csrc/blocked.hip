@@ -270,7 +270,41 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
     constexpr int PF = 1;
     V16 ra[PF][A_CH], rb[PF][B_CH];
 
+    // Interior tiles and steps (the common case) take branch-free 16-byte
+    // loads; the bounds and triangle checks only run at the edges.
+    const bool tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;
     auto load_step = [&](int64_t k0, int slot) {
+        const bool fast = tile_interior && k0 + BK <= p.Kr && (!p.a_lower || k0 + BK <= i0 + 1);
+        {
+            if (fast) {
+#pragma unroll
+                for (int e = 0; e < A_CH; ++e) {
+                    const int idx = tid + 256 * e;
+                    const int ic = idx % (kBM / VN), kl = idx / (kBM / VN);
+                    if constexpr (CPX) {
+                        // 16 bytes = VN/2 complex entries of complex column (k0+kl)/2;
+                        // real row 2kc holds (re, im), row 2kc+1 holds (-im, re)
+                        const int64_t kc = (k0 + kl) >> 1;
+                        const V16 raw = *(const V16 *)(p.A + (i0 / 2 + (int64_t)ic * (VN / 2)) + kc * p.lda);
+                        V16 v = raw;
+                        if (kl & 1) {
+#pragma unroll
+                            for (int t = 0; t < VN; t += 2) { v[t] = -raw[t + 1]; v[t + 1] = raw[t]; }
+                        }
+                        ra[slot][e] = v;
+                    } else {
+                        ra[slot][e] = *(const V16 *)(p.A + i0 + (int64_t)ic * VN + (k0 + kl) * p.lda);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < B_CH; ++e) {
+                    const int idx = tid + 256 * e;
+                    const int kc = idx % (BK / VN), jl = idx / (BK / VN);
+                    rb[slot][e] = *(const V16 *)(p.B + k0 + kc * VN + (j0 + jl) * p.ldb);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < A_CH; ++e) {
             const int idx = tid + 256 * e;
@@ -372,34 +406,36 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
         if (st + PF < nsteps) load_step((int64_t)(st + PF) * BK, PF == 2 ? (st & 1) : 0);
         const R *as = As[buf];
         const R *bs = Bs[buf];
-        // BK = NQ groups of LG*VN k values. The fragments of group q+1 are read
-        // from LDS before the MFMAs of group q are issued, so LDS latency
-        // overlaps matrix-core work.
+        // BK = NQ groups of LG*VN k values. All fragments of the step are read
+        // from LDS first; a scheduling barrier keeps the compiler from sinking
+        // each read to just before its MFMAs (which exposes LDS latency with a
+        // full wait per MFMA group). LDS returns in order, so the MFMAs start
+        // as soon as their own fragments have arrived.
         constexpr int NQ = BK / (LG * VN);
-        V16 bv[2][NBK];
-        R av[2][VN][NBK];
-        auto read_frag = [&](int q, int slot) {
+        V16 bv[NQ][NBK];
+        R av[NQ][VN][NBK];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
             const int kq = q * LG * VN + lg * VN;  // this lane group's first k in the group
 #pragma unroll
             for (int b = 0; b < NBK; ++b)
-                bv[slot][b] = *(const V16 *)&bs[(wj + b * BLK + lrow) * LDB_S + kq];
+                bv[q][b] = *(const V16 *)&bs[(wj + b * BLK + lrow) * LDB_S + kq];
 #pragma unroll
             for (int s = 0; s < VN; ++s)
 #pragma unroll
-                for (int a = 0; a < NBK; ++a) av[slot][s][a] = as[(kq + s) * LDA_S + wi + a * BLK + lrow];
-        };
-        read_frag(0, 0);
+                for (int a = 0; a < NBK; ++a) av[q][s][a] = as[(kq + s) * LDA_S + wi + a * BLK + lrow];
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            if (q + 1 < NQ) read_frag(q + 1, (q + 1) & 1);
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int s = 0; s < VN; ++s)
 #pragma unroll
                 for (int b = 0; b < NBK; ++b)
 #pragma unroll
                     for (int a = 0; a < NBK; ++a)
-                        acc[b][a] = mfma_op(bv[q & 1][b][s], av[q & 1][s][a], acc[b][a]);
-        }
+                        acc[b][a] = mfma_op(bv[q][b][s], av[q][s][a], acc[b][a]);
+        __builtin_amdgcn_sched_barrier(0);
         if (st + 1 < nsteps) store_step(buf ^ 1, PF == 2 ? ((st + 1) & 1) : 0);
         __syncthreads();
     }
