@@ -181,7 +181,7 @@ hsma_status diag_inv_impl(int64_t m, int32_t nb, int32_t ib, const T *A, int64_t
     if (ib < 1 || nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
     if (m == 0) return HSMA_STATUS_SUCCESS;
     if (!A || !invA) return HSMA_STATUS_INVALID_POINTER;
-    return hip_status(diag_invert<T>(m, nb, ib, A, lda, invA, (hipStream_t)stream));
+    return hip_status(diag_invert_any<T>(m, nb, ib, A, lda, invA, (hipStream_t)stream));
 }
 
 template <typename T>

@@ -148,6 +148,28 @@ static hipError_t diag_inv_launch(int64_t m, int nb, const T *A, int64_t lda, T 
 }
 
 template <typename T>
+static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T *invA, T *temp,
+                                  hipStream_t s);
+template <typename T>
+static bool blocked_inverse_applies(int64_t m, int nb);
+int64_t blocked_inverse_temp_elems(int64_t m, int nb);
+
+// Inversion of all diagonal blocks: the blocked-inverse formula where it
+// applies (temporaries allocated stream-ordered), else diag_inv_kernel.
+template <typename T>
+hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
+                           hipStream_t s)
+{
+    if (!blocked_inverse_applies<T>(m, nb)) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
+    void *tmp = nullptr;
+    hipError_t e = hipMallocAsync(&tmp, (size_t)blocked_inverse_temp_elems(m, nb) * sizeof(T), s);
+    if (e != hipSuccess) return e;
+    e = blocked_inverse<T>(m, nb, A, lda, invA, (T *)tmp, s);
+    const hipError_t ef = hipFreeAsync(tmp, s);
+    return e != hipSuccess ? e : ef;
+}
+
+template <typename T>
 hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, hipStream_t s)
 {
     // The identity tile of width ib is split into register-resident groups of
@@ -230,10 +252,18 @@ struct GemmArgs {
     int64_t Mr, N, Kr;
     R alpha, cscale;  // C = alpha * (cscale * C + A*B); cscale = beta / alpha, alpha != 0
     int a_lower;
+    // Batch (grid z): product z = g * bin + k uses A + g*sAo + k*sAi (elements
+    // of T) and B, C shifted likewise (real units).
+    int64_t bin;
+    int64_t sAi, sAo, sBi, sBo, sCi, sCo;
+    // Lower-triangular A: workgroup x computes row tiles x and (tiles-1-x),
+    // a light and a heavy one (K grows with the row), so all workgroups carry
+    // about the same number of K steps.
+    int pair;
 };
 
-template <typename T, bool VEC>
-__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
+template <typename T, bool VEC, bool PAIR>
+__global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
 {
     using R = typename traits<T>::real;
     using cfg = mfma_cfg<R>;
@@ -253,11 +283,16 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
     const int wave = tid >> 6;
     const int wi = (wave & 1) * 64;   // wave's row offset inside the tile (i)
     const int wj = (wave >> 1) * 64;  // wave's column offset (j)
-    const int64_t i0 = (int64_t)blockIdx.x * kBM;
+    int64_t i0 = (int64_t)blockIdx.x * kBM;  // row tile; reassigned per paired tile below
     const int64_t j0 = (int64_t)blockIdx.y * kBN;
+    {
+        const int64_t z = blockIdx.z, g = z / p.bin, k = z % p.bin;
+        p.A += g * p.sAo + k * p.sAi;
+        p.B += g * p.sBo + k * p.sBi;
+        p.C += g * p.sCo + k * p.sCi;
+    }
 
     int64_t kend = p.Kr;
-    if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
 
     // ---- staging of one K step: A as 16-byte chunks along i, B along k ----
     // A tile: BK x kBM reals = (kBM/VN) chunks per k row; chunks per thread:
@@ -272,7 +307,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 
     // Interior tiles and steps (the common case) take branch-free 16-byte
     // loads; the bounds and triangle checks only run at the edges.
-    const bool tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;
+    bool tile_interior = false;
     auto load_step = [&](int64_t k0, int slot) {
         const bool fast = tile_interior && k0 + BK <= p.Kr && (!p.a_lower || k0 + BK <= i0 + 1);
         {
@@ -385,6 +420,14 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
         else return lg + 4 * r;
     };
 
+    const int64_t ntile_rows = (p.Mr + kBM - 1) / kBM;
+    const int nrep = (PAIR && 2 * (int64_t)blockIdx.x + 1 != ntile_rows) ? 2 : 1;
+    for (int rep = 0; rep < (PAIR ? 2 : 1); ++rep) {
+    if (rep >= nrep) break;
+    i0 = (rep == 0 ? (int64_t)blockIdx.x : ntile_rows - 1 - (int64_t)blockIdx.x) * kBM;
+    kend = p.Kr;
+    if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
+    tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;
     typename cfg::acc_t acc[NBK][NBK];
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
@@ -456,15 +499,21 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
                     *cp = p.alpha * v;
                 }
             }
+    }  // paired row tiles
 }
 
+// Batched product: batch = nout * bin products; product z = g*bin + k uses
+// A + g*sAo + k*sAi, B + g*sBo + k*sBi, C + g*sCo + k*sCi (strides in elements).
 template <typename T>
-hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
-                int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
-                int64_t ldc, bool a_lower, hipStream_t s)
+static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
+                               const T *A, int64_t lda, int64_t sAi, int64_t sAo, const T *B,
+                               int64_t ldb, int64_t sBi, int64_t sBo, typename traits<T>::real beta,
+                               T *C, int64_t ldc, int64_t sCi, int64_t sCo, int64_t bin,
+                               int64_t batch, bool a_lower, hipStream_t s)
 {
     using R = typename traits<T>::real;
     constexpr int f = traits<T>::is_complex ? 2 : 1;
+    if (M == 0 || N == 0 || batch == 0) return hipSuccess;
     GemmArgs<T> p;
     p.A = A;
     p.lda = lda;
@@ -476,27 +525,126 @@ hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
     p.N = N;
     p.Kr = K * f;
     p.a_lower = a_lower ? 1 : 0;
+    p.pair = a_lower ? 1 : 0;
+    p.bin = bin > 0 ? bin : 1;
+    p.sAi = sAi; p.sAo = sAo;
+    p.sBi = sBi * f; p.sBo = sBo * f;
+    p.sCi = sCi * f; p.sCo = sCo * f;
     if (alpha == R(0)) {
         // C = beta * C with beta in {0, 1}: nothing to multiply
         if (beta != R(0)) return hipSuccess;
         p.alpha = R(1);
         p.cscale = R(0);
-        K = 0;
         p.Kr = 0;
     } else {
         p.alpha = alpha;
         p.cscale = beta / alpha;
     }
-    const int64_t gx = (p.Mr + kBM - 1) / kBM, gy = (N + kBN - 1) / kBN;
-    if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
-    // 16-byte loads need 16-byte aligned columns of A (real types) and B.
-    const bool vec = (uintptr_t)A % 16 == 0 && (uintptr_t)B % 16 == 0 &&
-                     (lda * (int64_t)sizeof(T)) % 16 == 0 && (ldb * (int64_t)sizeof(T)) % 16 == 0;
-    if (vec)
-        hipLaunchKernelGGL((gemm_kernel<T, true>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((gemm_kernel<T, false>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, p);
+    int64_t gx = (p.Mr + kBM - 1) / kBM;
+    if (p.pair) gx = (gx + 1) / 2;
+    const int64_t gy = (N + kBN - 1) / kBN;
+    if (gx > 0x7fffffff || gy > 65535 || batch > 65535) return hipErrorInvalidConfiguration;
+    // 16-byte loads need 16-byte aligned columns of A and B (every batch member).
+    const int64_t sz = (int64_t)sizeof(T);
+    const bool vec = (uintptr_t)A % 16 == 0 && (uintptr_t)B % 16 == 0 && (lda * sz) % 16 == 0 &&
+                     (ldb * sz) % 16 == 0 && (sAi * sz) % 16 == 0 && (sAo * sz) % 16 == 0 &&
+                     (sBi * sz) % 16 == 0 && (sBo * sz) % 16 == 0;
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)batch);
+    if (p.pair) {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, true>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<T, false, true>), grid, dim3(256), 0, s, p);
+    } else {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, false>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<T, false, false>), grid, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
+                int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
+                int64_t ldc, bool a_lower, hipStream_t s)
+{
+    return gemm_batched<T>(M, N, K, alpha, A, lda, 0, 0, B, ldb, 0, 0, beta, C, ldc, 0, 0, 1, 1,
+                           a_lower, s);
+}
+
+// ---------------------------------------------------------------------------
+// Diagonal-block inversion by the blocked-inverse formula
+//
+// The HSMA-TRSM paper's two-level blocking reuses the small-scale solver for
+// the small diagonal sub-blocks and turns the inter-sub-block updates into
+// matrix multiplies through the blocked matrix inversion formula:
+//
+//   [L11   0 ]^-1   [ L11^-1               0     ]
+//   [L21  L22]    = [ -L22^-1 L21 L11^-1   L22^-1 ]
+//
+// Here: (1) every 64 x 64 diagonal sub-block is inverted by the small-regime
+// lane-per-column kernel against an identity right-hand side, in place in
+// invA; (2) sub-blocks are merged pairwise, 64 -> 128 -> ... -> N_B, each level
+// two batched GEMMs over all pairs of all diagonal blocks:
+//   T = L21 L11^-1,   (inverse)21 = -L22^-1 T   (L22^-1 lower: zero tiles skipped).
+// Used when m is a multiple of N_B and N_B of 64; otherwise diag_inv_kernel.
+
+template <typename T>
+__global__ void __launch_bounds__(256) identity_kernel(T *out, int64_t total, int64_t nb)
+{
+    T one = zero_of(T());
+    if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t within = e % (nb * nb);
+        out[e] = (within % nb == within / nb) ? one : zero_of(T());
+    }
+}
+
+int64_t blocked_inverse_temp_elems(int64_t m, int nb)
+{
+    const int64_t nt = (m + nb - 1) / nb;
+    return nt * (int64_t)nb * nb / 4 + 1;
+}
+
+template <typename T>
+static bool blocked_inverse_applies(int64_t m, int nb)
+{
+    return m % nb == 0 && nb % 64 == 0 && nb >= 128;
+}
+
+template <typename T>
+static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T *invA, T *temp,
+                                  hipStream_t s)
+{
+    using R = typename traits<T>::real;
+    const int64_t nt = m / nb;
+    const int64_t total = nt * (int64_t)nb * nb;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(identity_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, invA, total,
+                       (int64_t)nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    T one = zero_of(T());
+    if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
+    // (1) 64 x 64 diagonal sub-blocks: problem z = t * (nb/64) + k
+    e = small_colane2<T>(64, one, A, lda, 64 * (lda + 1), nb * (lda + 1), invA, nb,
+                         64 * ((int64_t)nb + 1), (int64_t)nb * nb, nb / 64, m / 64, s);
+    if (e != hipSuccess) return e;
+    // (2) merge pairs of s x s inverses
+    for (int64_t sz = 64; sz < nb; sz *= 2) {
+        const int64_t pairs = nb / (2 * sz), batch = nt * pairs;
+        // T = L21 * inv11
+        e = gemm_batched<T>(sz, sz, sz, R(1), A + sz, lda, 2 * sz * (lda + 1), (int64_t)nb * (lda + 1),
+                            invA, nb, 2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, R(0), temp, sz,
+                            sz * sz, pairs * sz * sz, pairs, batch, false, s);
+        if (e != hipSuccess) return e;
+        // inv21 = -inv22 * T
+        e = gemm_batched<T>(sz, sz, sz, R(-1), invA + sz * ((int64_t)nb + 1), nb,
+                            2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, temp, sz, sz * sz,
+                            pairs * sz * sz, R(0), invA + sz, nb, 2 * sz * ((int64_t)nb + 1),
+                            (int64_t)nb * nb, pairs, batch, true, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -515,7 +663,10 @@ __global__ void __launch_bounds__(256) copy_kernel(const T *__restrict__ W, int6
 int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
 {
     const int64_t nt = (m + nb - 1) / nb;
-    return nt * nb * nb + (int64_t)nb * n;
+    int64_t w = (int64_t)nb * n;
+    const int64_t t = blocked_inverse_temp_elems(m, nb);
+    if (t > w) w = t;  // the merge temporaries live in W before W is used
+    return nt * nb * nb + w;
 }
 
 template <typename T>
@@ -526,7 +677,8 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     const int64_t nt = (m + nb - 1) / nb;
     T *invA = work;
     T *W = work + nt * nb * nb;
-    hipError_t e = diag_invert<T>(m, nb, ib, A, lda, invA, s);
+    hipError_t e = blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, W, s)
+                                                     : diag_invert<T>(m, nb, ib, A, lda, invA, s);
     for (int64_t t = 0; t < nt && e == hipSuccess; ++t) {
         const int64_t r0 = t * nb;
         const int64_t rb = m - r0 < nb ? m - r0 : nb;
@@ -550,6 +702,7 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
 
 #define HSMA_INST(T)                                                                              \
     template hipError_t diag_invert<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t);  \
+    template hipError_t diag_invert_any<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t); \
     template hipError_t gemm<T>(int64_t, int64_t, int64_t, typename traits<T>::real, const T *,    \
                                 int64_t, const T *, int64_t, typename traits<T>::real, T *,       \
                                 int64_t, bool, hipStream_t);                                      \

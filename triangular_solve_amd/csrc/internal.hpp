@@ -20,6 +20,13 @@ template <typename T>
 hipError_t small_colane(int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA, T *B,
                         int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s);
 
+// Same with a two-level batch: problem z = g * per + k uses A + g*strideA2 +
+// k*strideA and B + g*strideB2 + k*strideB.
+template <typename T>
+hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
+                         int64_t strideA2, T *B, int64_t ldb, int64_t strideB, int64_t strideB2,
+                         int64_t per, int64_t batch, hipStream_t s);
+
 // B := alpha*B, or B := 0 when set_zero (column-major, batched).
 template <typename T>
 hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB, int64_t batch,
@@ -29,6 +36,12 @@ hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB
 template <typename T>
 hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
                        hipStream_t s);
+
+// Same, choosing the blocked-inverse formula (small solver + batched GEMMs)
+// when m is a multiple of nb and nb of 64 (nb >= 128).
+template <typename T>
+hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
+                           hipStream_t s);
 
 // C = beta*C + alpha*A*B on the matrix cores (beta in {0, 1}); a_lower: A is
 // lower triangular (M == K) and its upper tiles are skipped.

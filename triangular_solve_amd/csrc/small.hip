@@ -393,7 +393,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
                                                          int64_t strideA, T *__restrict__ B,
                                                          int64_t ldb, int64_t strideB, int64_t n,
                                                          int64_t nchunks, int64_t items, T alpha,
-                                                         T alpha_inv)
+                                                         T alpha_inv, int64_t per, int64_t strideA2,
+                                                         int64_t strideB2)
 {
     constexpr int M = 64;
     constexpr int P = M / NPANEL;
@@ -408,10 +409,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     const int64_t c = cfirst + lane;
     const bool live = c < n;
 
-    const T *Ap = A + prob * strideA;
+    // problem prob = g * per + k lives at A + g*strideA2 + k*strideA (B alike)
+    const int64_t pg = prob / per, pk = prob % per;
+    const T *Ap = A + pg * strideA2 + pk * strideA;
     // Lanes past n work on a copy of the wave's first column (always valid)
     // and never store, so loads need no guard.
-    T *Bc0 = B + prob * strideB + cfirst * ldb;
+    T *Bc0 = B + pg * strideB2 + pk * strideB + cfirst * ldb;
 
     PanelState<T, P> st;
     st.a4 = (cptr<T>)Ap;
@@ -459,6 +462,15 @@ template <typename T>
 hipError_t small_colane(int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA, T *B,
                         int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s)
 {
+    return small_colane2<T>(n, alpha, A, lda, strideA, 0, B, ldb, strideB, 0, batch, batch, s);
+}
+
+template <typename T>
+hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
+                         int64_t strideA2, T *B, int64_t ldb, int64_t strideB, int64_t strideB2,
+                         int64_t per, int64_t batch, hipStream_t s)
+{
+    if (per <= 0) per = 1;
     const int64_t nchunks = (n + 63) / 64;
     const int64_t items = nchunks * batch;
     const int64_t blocks = (items + 3) / 4;
@@ -479,7 +491,8 @@ hipError_t small_colane(int64_t n, T alpha, const T *A, int64_t lda, int64_t str
     size_t lds = 0;
     if (per_cu >= 3 && per_cu < 8) lds = ((size_t)(160 * 1024) / (size_t)per_cu) & ~(size_t)1023;
     hipLaunchKernelGGL((colane_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), lds, s, A, lda,
-                       strideA, B, ldb, strideB, n, nchunks, items, alpha, alpha_inv);
+                       strideA, B, ldb, strideB, n, nchunks, items, alpha, alpha_inv, per, strideA2,
+                       strideB2);
     return hipGetLastError();
 }
 
@@ -524,6 +537,8 @@ hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB
                                          hipStream_t);                                             \
     template hipError_t small_colane<T>(int64_t, T, const T *, int64_t, int64_t, T *, int64_t,     \
                                         int64_t, int64_t, hipStream_t);                            \
+    template hipError_t small_colane2<T>(int64_t, T, const T *, int64_t, int64_t, int64_t, T *,    \
+                                         int64_t, int64_t, int64_t, int64_t, int64_t, hipStream_t);\
     template hipError_t scale_matrix<T>(T *, int64_t, int64_t, int64_t, int64_t, int64_t, T, bool, \
                                         hipStream_t);
 HSMA_INST(float)
