@@ -59,7 +59,11 @@ def test_shapes(hs, dtype, m, n):
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_padded_leading_dims_alpha_and_shared_a(hs, dtype):
     cplx = dtype.startswith("c")
-    for (m, n, lda, ldb) in [(64, 64, 70, 67), (64, 40, 64, 65), (20, 9, 33, 21)]:
+    # odd ldb: B's columns are not 16-byte aligned (lane-per-row kernel for
+    # the real and c64 types); ldb 68 / 72: aligned padding, lane-per-column
+    # kernel with its LDS tile (n = 100: a partial second group of columns)
+    for (m, n, lda, ldb) in [(64, 64, 70, 67), (64, 40, 64, 65), (20, 9, 33, 21),
+                             (64, 64, 70, 68), (64, 100, 66, 72)]:
         for alpha in [2.0, -0.5] + ([0.3 + 0.7j] if cplx else []):
             say("padded", dtype, m, n, lda, ldb, alpha)
             A, B = colmajor_inputs(dtype, m, n, 4, lda=lda, ldb=ldb, seed=7)

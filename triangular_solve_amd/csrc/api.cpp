@@ -115,10 +115,14 @@ template <typename T>
 hipError_t small_path(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
                       T *B, int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s)
 {
-    // The lane-per-column kernel needs the full 64 rows and enough columns to
-    // fill a wavefront; otherwise the lane-per-row kernel.
-    if (m == 64 && n >= 32)
-        return small_colane<T>(n, alpha, A, lda, strideA, B, ldb, strideB, batch, s);
+    // The lane-per-column kernel needs the full 64 rows, enough columns to
+    // fill a wavefront and 16-byte aligned columns of B; otherwise the
+    // lane-per-row kernel.
+    const int64_t sb = batch > 1 ? strideB : 0;
+    const bool aligned = ((uintptr_t)B & 15) == 0 && ((ldb * (int64_t)sizeof(T)) & 15) == 0 &&
+                         ((sb * (int64_t)sizeof(T)) & 15) == 0;
+    if (m == 64 && n >= 32 && aligned)
+        return small_colane<T>(n, alpha, A, lda, strideA, B, ldb, sb, batch, s);
     return small_rowlane<T>(A, 1, lda, strideA, 0, B, 1, ldb, strideB, 0, B, 1, ldb, strideB, 0,
                             m, n, batch, 1, alpha, s);
 }

@@ -217,6 +217,17 @@ __device__ __forceinline__ T ld_uniform(cptr<T> p, int idx)
     }
 }
 
+// 16 bytes as four dwords: the unit of B's tile traffic.
+typedef int v4i __attribute__((ext_vector_type(4)));
+using lptr = __attribute__((address_space(3))) char *;
+using lptr_v4i = __attribute__((address_space(3))) v4i *;
+
+// Per-wave LDS tile of 64 columns x one 128-byte line; the 16-byte pad of
+// the column stride keeps both the line-wise and the column-wise 16-byte
+// accesses free of bank conflicts.
+constexpr int kTileCol = 144;
+constexpr int kTileBytes = 64 * kTileCol;
+
 // Empty asm that makes v look modified after `dep` is available: values
 // derived from v cannot be computed before dep. Emits no instruction.
 template <typename V, typename T>
@@ -286,6 +297,71 @@ struct PanelPlan {
 template <typename T>
 constexpr int kBatch = (int)(256 / sizeof(T));
 
+// Prefetch distance of A's coefficients, in stream coefficients. Measured
+// on MI355X (4096 problems of 64 x 64) from 32 to 768 coefficients: 96 is
+// best for f32, f64 and c64, 48 for c128; further ahead loses (the lines
+// compete for L2 with the other resident waves' lines).
+template <typename T>
+constexpr int kAhead = sizeof(T) == 16 ? 48 : 96;
+
+// L2 prefetch schedule of a panel's coefficient stream. Every non-empty
+// column segment s (one column of A, rows [lo, hi) of the panel) has its
+// cache lines fetched by a vector load at batch tb(s), the batch in which
+// the stream reaches AH coefficients before the segment, and the load's
+// result is retired at batch cb(s), the batch that reads the segment with
+// scalar loads. The scalar loads then find the lines in L2 instead of
+// waiting on HBM with a full wait each. Both tb and cb grow with s, so each
+// batch handles a contiguous range of segments.
+template <int P, int R0, int G, int AH>
+struct TouchPlan {
+    using Plan = PanelPlan<P, R0, G>;
+    static constexpr int NS = R0 + P - 1;
+    struct Seg {
+        int col, lo, hi;
+    };
+    struct Table {
+        Seg sg[NS > 0 ? NS : 1];
+        int tfirst[Plan::NP + 1];  // segments touched at batch b: [tfirst[b], tfirst[b+1])
+        int cfirst[Plan::NP + 1];  // segments retired at batch b: [cfirst[b], cfirst[b+1])
+    };
+    static constexpr Table build()
+    {
+        Table t{};
+        constexpr auto &pt = Plan::T;
+        int bpos[Plan::NP + 1] = {};
+        int tb[NS > 0 ? NS : 1] = {}, cb[NS > 0 ? NS : 1] = {};
+        int pos = 0, ns = 0;
+        for (int b = 0; b < pt.nbatch; ++b) {
+            bpos[b] = pos;
+            for (int i = pt.bfirst[b]; i < pt.bfirst[b + 1]; ++i) {
+                const auto &pc = pt.pc[i];
+                if (pc.first && pc.hi > pc.lo) {
+                    // a segment runs over consecutive pieces of one column
+                    int hi = pc.hi;
+                    for (int k = i + 1; k < Plan::NP && !pt.pc[k].first; ++k) hi = pt.pc[k].hi;
+                    t.sg[ns] = Seg{pc.col, pc.lo, hi};
+                    cb[ns] = b;
+                    int at = 0;
+                    while (at + 1 < pt.nbatch && pos - AH >= bpos[at + 1] && at + 1 <= b) ++at;
+                    tb[ns] = at;
+                    ++ns;
+                }
+                pos += pc.hi - pc.lo;
+            }
+        }
+        bpos[pt.nbatch] = pos;
+        for (int b = 0; b <= pt.nbatch; ++b) {
+            int f = 0, c = 0;
+            while (f < ns && tb[f] < b) ++f;
+            while (c < ns && cb[c] < b) ++c;
+            t.tfirst[b] = f;
+            t.cfirst[b] = c;
+        }
+        return t;
+    }
+    static constexpr Table T = build();
+};
+
 // Per-panel state shared by the batch recursion below.
 template <typename T, int P>
 struct PanelState {
@@ -294,9 +370,93 @@ struct PanelState {
     cptr<T> a4;   // A of this problem (scalar loads)
     int64_t lda;
     T *Bc;        // this lane's column of B (read back finished rows)
+    T *Bw;        // first of the wave's 64 columns of B
+    int64_t ldb;
+    int ncol;     // columns of the wave that exist (<= 64)
+    lptr tile;    // this wave's LDS tile
+    int lane128;  // lane * 128: this lane's line of a prefetched segment
+    int tv[64];   // results of the segments' prefetch loads, retired later
     T myinv;      // 1/a_ll of this lane's row index l
     T alpha_inv;
 };
+
+// Rows [r0, r0 + P) of the wave's columns into st.w, lane = column. Each
+// 128-byte line of a column is fetched by 8 lanes with 16-byte loads (a
+// lane-per-column load would touch 64 lines per instruction), written to
+// the tile and read back one column per lane. The next tile's loads are in
+// flight while the current one is transposed.
+template <typename T, int P>
+__device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int r0)
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    constexpr int L = 128 / (int)sizeof(T);
+    constexpr int NCH = P / L;
+    static_assert(P % L == 0, "panel rows must be whole lines");
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+    int64_t goff[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        int col = q * 8 + (lane >> 3);
+        col = col < st.ncol ? col : st.ncol - 1;  // duplicates of a valid column
+        goff[q] = col * st.ldb + r0 + sub * V;
+    }
+    v4i cur[8], nxt[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cur[q] = *(const gptr<v4i>)(bw + goff[q]);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch + 1 < NCH) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) nxt[q] = *(const gptr<v4i>)(bw + goff[q] + (ch + 1) * L);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            *(lptr_v4i)(st.tile + (q * 8 + (lane >> 3)) * kTileCol + sub * 16) = cur[q];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const v4i v = *(const lptr_v4i)(st.tile + lane * kTileCol + k * 16);
+            T t[V];
+            __builtin_memcpy(t, &v, 16);
+#pragma unroll
+            for (int e = 0; e < V; ++e) st.w[ch * L + k * V + e] = t[e];
+        }
+        if (ch + 1 < NCH) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
+        }
+    }
+}
+
+// alpha * st.w into rows [r0, r0 + P) of the wave's columns, the reverse
+// of load_panel (columns past ncol are not written).
+template <typename T, int P>
+__device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, int r0, T alpha)
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    constexpr int L = 128 / (int)sizeof(T);
+    constexpr int NCH = P / L;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            T t[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) t[e] = mul(alpha, st.w[ch * L + k * V + e]);
+            v4i v;
+            __builtin_memcpy(&v, t, 16);
+            *(lptr_v4i)(st.tile + lane * kTileCol + k * 16) = v;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int col = q * 8 + (lane >> 3);
+            const v4i v = *(const lptr_v4i)(st.tile + col * kTileCol + sub * 16);
+            if (col < st.ncol) *(gptr<v4i>)(bw + col * st.ldb + r0 + ch * L + sub * V) = v;
+        }
+    }
+}
 
 // Scalar loads of the pieces [Q, Q1) of a batch into cb.
 template <typename T, int P, int R0, int G, int Q, int Q1>
@@ -346,45 +506,74 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
     }
 }
 
-// Batches [Bi, nbatch) of the panel at rows R0: fetch, one wait, update.
-template <typename T, int P, int R0, int G, int Bi>
+// L2 prefetch of segments [S, S1): lane l loads one dword of the l-th
+// 128-byte line from the line holding the segment's first coefficient on;
+// the buffer's range check (the records end at the segment's last byte)
+// turns the lanes past the segment into no-ops.
+template <typename T, int P, int R0, int G, int AH, int S, int S1>
+__device__ __forceinline__ void batch_touch(PanelState<T, P> &st, cptr<T> ap)
+{
+    if constexpr (S < S1) {
+        constexpr auto sg = TouchPlan<P, R0, G, AH>::T.sg[S];
+        const uint64_t first = (uint64_t)(ap + (R0 + sg.lo + (int64_t)sg.col * st.lda));
+        const uint64_t line = first & ~(uint64_t)127;
+        const int bytes = (int)(first - line) + (sg.hi - sg.lo) * (int)sizeof(T);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)line, (short)0, bytes, 0x00020000);
+        st.tv[S] = __builtin_amdgcn_raw_buffer_load_b32(rs, st.lane128, 0, 0);
+        batch_touch<T, P, R0, G, AH, S + 1, S1>(st, ap);
+    }
+}
+
+// Retire the prefetch loads of segments [S, S1) (waits for them if needed).
+template <typename T, int P, int S, int S1>
+__device__ __forceinline__ void batch_retire(PanelState<T, P> &st)
+{
+    if constexpr (S < S1) {
+        asm volatile("" ::"v"(st.tv[S]));
+        batch_retire<T, P, S + 1, S1>(st);
+    }
+}
+
+// Batches [Bi, nbatch) of the panel at rows R0: prefetch ahead, fetch, one
+// wait, update.
+template <typename T, int P, int R0, int G, int AH, int Bi>
 __device__ __forceinline__ void run_batches(PanelState<T, P> &st)
 {
     using Plan = PanelPlan<P, R0, G>;
+    using TP = TouchPlan<P, R0, G, AH>;
     if constexpr (Bi < Plan::T.nbatch) {
         constexpr int p0 = Plan::T.bfirst[Bi], p1 = Plan::T.bfirst[Bi + 1];
         // fetch this batch once the previous one has been consumed
         cptr<T> ap = st.a4;
         order_after(ap, st.x);
+        batch_touch<T, P, R0, G, AH, TP::T.tfirst[Bi], TP::T.tfirst[Bi + 1]>(st, ap);
         T cb[G];
         batch_load<T, P, R0, G, p0, p1>(cb, ap, st.lda);
+        batch_retire<T, P, TP::T.cfirst[Bi], TP::T.cfirst[Bi + 1]>(st);
         batch_compute<T, P, R0, G, p0, p1>(st, cb);
         __builtin_amdgcn_sched_barrier(0);
-        run_batches<T, P, R0, G, Bi + 1>(st);
+        run_batches<T, P, R0, G, AH, Bi + 1>(st);
     }
 }
 
 template <typename T, int P, int NPANEL, int PI>
-__device__ __forceinline__ void run_panels(PanelState<T, P> &st, bool live, T alpha,
+__device__ __forceinline__ void run_panels(PanelState<T, P> &st, T alpha,
                                            typename traits<T>::real wlast)
 {
     if constexpr (PI < NPANEL) {
         constexpr int r0 = PI * P;
         // a later panel's rows are loaded only after the earlier panel is done
-        const gptr<T> bp = global_after(st.Bc, wlast);
-#pragma unroll
-        for (int r = 0; r < P; ++r) st.w[r] = ld_global<T>(bp, r0 + r);
+        const gptr<T> bw = global_after(st.Bw, wlast);
+        load_panel<T, P>(st, bw, r0);
         st.x = zero_of(T());
-        run_batches<T, P, r0, kBatch<T>, 0>(st);
+        run_batches<T, P, r0, kBatch<T>, kAhead<T>, 0>(st);
         // The solve ran on B itself; alpha is applied to X on the way out
         // (A (alpha^{-1} X) = B has the same substitution with alpha factored out).
-        if (live) {
-#pragma unroll
-            for (int r = 0; r < P; ++r) st.Bc[r0 + r] = mul(alpha, st.w[r]);
-        }
+        store_panel<T, P>(st, bw, r0, alpha);
         typename traits<T>::real wl;
         if constexpr (traits<T>::is_complex) wl = st.w[P - 1].re; else wl = st.w[P - 1];
-        run_panels<T, P, NPANEL, PI + 1>(st, live, alpha, wl);
+        run_panels<T, P, NPANEL, PI + 1>(st, alpha, wl);
     }
 }
 
@@ -396,6 +585,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
                                                          T alpha_inv, int64_t per, int64_t strideA2,
                                                          int64_t strideB2)
 {
+    extern __shared__ __attribute__((aligned(16))) char colane_lds[];
     constexpr int M = 64;
     constexpr int P = M / NPANEL;
     const int lane = threadIdx.x & 63;
@@ -412,35 +602,23 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     // problem prob = g * per + k lives at A + g*strideA2 + k*strideA (B alike)
     const int64_t pg = prob / per, pk = prob % per;
     const T *Ap = A + pg * strideA2 + pk * strideA;
-    // Lanes past n work on a copy of the wave's first column (always valid)
-    // and never store, so loads need no guard.
+    // Lanes past n work on a copy of a valid column and never store, so
+    // loads need no guard.
     T *Bc0 = B + pg * strideB2 + pk * strideB + cfirst * ldb;
 
     PanelState<T, P> st;
     st.a4 = (cptr<T>)Ap;
     st.lda = lda;
     st.Bc = Bc0 + (live ? lane : 0) * ldb;
+    st.Bw = Bc0;
+    st.ldb = ldb;
+    st.ncol = (int)(n - cfirst < 64 ? n - cfirst : 64);
+    st.tile = (lptr)colane_lds + wave * kTileBytes;
     st.alpha_inv = alpha_inv;
 
-    // Warm L2 with this problem's triangle: lane l touches every cache line
-    // of column l from the diagonal down, one dword per line, so the scalar
-    // loads below find the coefficients in L2 instead of HBM.
-    constexpr int kLine = 128 / (int)sizeof(T);  // elements per 128-byte line
-    constexpr int kTouch = 64 / kLine + 2;
-    uint32_t touch[kTouch];
-    {
-        const uint32_t *colp = (const uint32_t *)(Ap + lane * lda);
-#pragma unroll
-        for (int q = 0; q < kTouch; ++q) {
-            int row = lane + q * kLine;
-            row = row < 63 ? row : 63;
-            touch[q] = colp[row * (int)(sizeof(T) / 4)];
-        }
-    }
+    st.lane128 = lane * 128;
     st.myinv = recip(Ap[lane + lane * lda]);
-    run_panels<T, P, NPANEL, 0>(st, live, alpha, typename traits<T>::real(0));
-#pragma unroll
-    for (int q = 0; q < kTouch; ++q) asm volatile("" ::"v"(touch[q]));
+    run_panels<T, P, NPANEL, 0>(st, alpha, typename traits<T>::real(0));
 }
 
 // Compute units of the current device (cached per device).
@@ -484,12 +662,20 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
     constexpr int NP = sizeof(T) == 16 ? 2 : 1;
     // Earlier panels' rows are read back from B already scaled by alpha.
     const T alpha_inv = host_recip(alpha);
-    // Spread the workgroups evenly over the CUs: left alone, the dispatcher
-    // may pack up to the occupancy limit onto fewer CUs. Reserving LDS (the
-    // kernel uses none) caps the workgroups per CU at the even share.
+    // The 16-byte tile accesses need 16-byte aligned columns.
+    if (((uintptr_t)B & 15) != 0 || ((ldb * (int64_t)sizeof(T)) & 15) != 0 ||
+        ((strideB * (int64_t)sizeof(T)) & 15) != 0 || ((strideB2 * (int64_t)sizeof(T)) & 15) != 0)
+        return hipErrorInvalidValue;
+    // One tile per wave. Spread the workgroups evenly over the CUs: left
+    // alone, the dispatcher may pack up to the occupancy limit onto fewer
+    // CUs; reserving more LDS than the tiles need caps the workgroups per CU
+    // at the even share.
     const int64_t per_cu = (blocks + num_cus() - 1) / num_cus();
-    size_t lds = 0;
-    if (per_cu >= 3 && per_cu < 8) lds = ((size_t)(160 * 1024) / (size_t)per_cu) & ~(size_t)1023;
+    size_t lds = 4 * kTileBytes;
+    if (per_cu >= 3 && per_cu < 8) {
+        const size_t share = ((size_t)(160 * 1024) / (size_t)per_cu) & ~(size_t)1023;
+        if (share > lds) lds = share;
+    }
     hipLaunchKernelGGL((colane_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), lds, s, A, lda,
                        strideA, B, ldb, strideB, n, nchunks, items, alpha, alpha_inv, per, strideA2,
                        strideB2);
