@@ -257,10 +257,15 @@ def counter_workload(hs, torch):
     log("counter workload done")
 
 
-# HBM bytes per launch of the batched small kernel from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE (profiles/colane_batched64_hbm_traffic.md), valid only for the
-# kernel source they were taken on: keyed by the SHA-256 of small.hip.
-MEASURED_TRAFFIC = {}
+# HBM bytes per launch of the batched small kernel (4096 problems of 64 x 64),
+# from rocprofv3 FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00, the factors a 1 GiB
+# device copy reads for the two counters (profiles/colane_batched64_hbm_traffic.md).
+# Valid only for the kernel source they were taken on: keyed by the SHA-256 of
+# small.hip.
+MEASURED_TRAFFIC = {
+    "8cf4fc611bdc3e96242917c50355464373caaaba1b7d47cf6578b1882645b373": {
+        "f32": 218264576, "f64": 385543168, "c64": 388154368, "c128": 1030157312},
+}
 
 
 def measured_traffic(dtype):
