@@ -219,3 +219,38 @@ def test_full_size_sampled_columns(hs, dtype):
     Bs = B[0, cols].T
     Xo = oracle.trsm(Av, Bs)                                         # (m, 64)
     assert rel_err(Xg.T[None], Xo[None]) <= TOL_LARGE[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c128"])
+def test_largest_size_sampled_columns_and_residual(hs, dtype):
+    """m = n = 16384 (the largest blocked size), one call with the table N_B:
+    64 seeded columns against the oracle, and the scaled residual of the whole
+    solution ||tril(A) X - B||_F / (||tril(A)||_F ||X||_F) <= 10 m eps, formed
+    with plain torch products in double precision on the GPU."""
+    import torch
+    m = n = 16384
+    say("full 16384", dtype)
+    A = synth.tri(dtype, m, seed=0x5EED0004)
+    B = synth.rhs(dtype, m, n, seed=0x5EED0004 + 1)
+    dA, dB = to_dev(A), to_dev(B)
+    assert hs.entry("trsm", dtype)(m, n, 1.0, dA, m, dB, m) == hs.SUCCESS
+    torch.cuda.synchronize()
+    cols = synth.pick_columns(n, 64, seed=0x5EED0004)
+    Xg = dB[0, torch.from_numpy(cols).cuda()].cpu().numpy()          # (64, m)
+    # residual: storage is column-major, so dA[0] holds A^T and dB[0] holds X^T
+    wide = torch.complex128 if dtype.startswith("c") else torch.float64
+    AT = torch.nan_to_num(dA[0].to(wide), nan=0.0)
+    del dA
+    AT = torch.triu(AT)                                              # tril(A)^T
+    XT = dB[0].to(wide)
+    del dB
+    RT = XT @ AT                                                     # (tril(A) X)^T
+    RT -= torch.from_numpy(B[0]).cuda().to(wide)
+    num = torch.linalg.vector_norm(RT).item()
+    den = torch.linalg.vector_norm(AT).item() * torch.linalg.vector_norm(XT).item()
+    del AT, XT, RT
+    torch.cuda.empty_cache()
+    say("residual", num / den)
+    assert num / den <= 10 * m * EPS[dtype]
+    Xo = oracle.trsm(A[0].T, B[0, cols].T)                           # (m, 64)
+    assert rel_err(Xg.T[None], Xo[None]) <= TOL_LARGE[dtype]
