@@ -24,8 +24,11 @@
  *     stream). They return once the work is enqueued. A kernel fault surfaces
  *     at the caller's next synchronisation.
  *   - Workspace for the blocked path is allocated stream-ordered on `stream`
- *     (hipMallocAsync / hipFreeAsync), so calls on different streams do not
- *     share memory.
+ *     (hipMallocFromPoolAsync / hipFreeAsync), so calls on different streams
+ *     do not share memory. It comes from a memory pool the library creates
+ *     once per device and keeps until the process ends; freed workspace stays
+ *     in that pool for the next call (its size is at most the largest
+ *     workspace used so far) instead of being returned to the driver.
  *   - No singularity check: a zero or NaN diagonal entry produces inf/NaN
  *     under IEEE rules (the SOLVE_TRI review in llama.cpp PR #17457 dropped
  *     its zero-pivot guard for the same reason).

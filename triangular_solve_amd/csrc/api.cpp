@@ -17,6 +17,58 @@
 #include "internal.hpp"
 
 namespace hsma {
+
+// ---------------------------------------------------------------------------
+// Workspace pool: one stream-ordered memory pool per device, owned by the
+// library for the life of the process. Its release threshold is unlimited,
+// so memory freed at the end of a call stays mapped for the next one; with
+// the default pool (threshold 0) every synchronisation hands it back to the
+// driver and the next call maps it again.
+
+namespace {
+constexpr int kMaxDevices = 64;
+hipMemPool_t g_pool[kMaxDevices] = {};
+std::mutex g_pool_mutex;
+
+hipError_t device_pool(int dev, hipMemPool_t *out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    if (!g_pool[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        hipError_t e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return e;
+        }
+        g_pool[dev] = pool;
+    }
+    *out = g_pool[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t workspace_alloc(void **p, size_t bytes, hipStream_t s)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipMemPool_t pool = nullptr;
+    e = device_pool(dev, &pool);
+    if (e != hipSuccess) return e;
+    return hipMallocFromPoolAsync(p, bytes, pool, s);
+}
+
+hipError_t workspace_free(void *p, hipStream_t s) { return hipFreeAsync(p, s); }
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -160,7 +212,7 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
 
     const int64_t welems = blocked_workspace_elems(m, n, nb);
     void *work = nullptr;
-    if (hipMallocAsync(&work, (size_t)welems * sizeof(T), s) != hipSuccess || !work) {
+    if (workspace_alloc(&work, (size_t)welems * sizeof(T), s) != hipSuccess || !work) {
         (void)hipGetLastError();
         return HSMA_STATUS_ALLOC_FAILED;
     }
@@ -168,7 +220,7 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     if (!is_one(alpha)) e = scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, false, s);
     for (int64_t b = 0; b < batch && e == hipSuccess; ++b)
         e = blocked_solve<T>(m, n, nb, ib, A + b * strideA, lda, B + b * strideB, ldb, (T *)work, s);
-    const hipError_t ef = hipFreeAsync(work, s);
+    const hipError_t ef = workspace_free(work, s);
     if (e != hipSuccess || ef != hipSuccess) return HSMA_STATUS_HIP_ERROR;
     return HSMA_STATUS_SUCCESS;
 }

@@ -162,10 +162,10 @@ hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T
 {
     if (!blocked_inverse_applies<T>(m, nb)) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
     void *tmp = nullptr;
-    hipError_t e = hipMallocAsync(&tmp, (size_t)blocked_inverse_temp_elems(m, nb) * sizeof(T), s);
+    hipError_t e = workspace_alloc(&tmp, (size_t)blocked_inverse_temp_elems(m, nb) * sizeof(T), s);
     if (e != hipSuccess) return e;
     e = blocked_inverse<T>(m, nb, A, lda, invA, (T *)tmp, s);
-    const hipError_t ef = hipFreeAsync(tmp, s);
+    const hipError_t ef = workspace_free(tmp, s);
     return e != hipSuccess ? e : ef;
 }
 

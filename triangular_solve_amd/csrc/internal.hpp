@@ -32,6 +32,11 @@ template <typename T>
 hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB, int64_t batch,
                         T alpha, bool set_zero, hipStream_t s);
 
+// Stream-ordered workspace from the library's memory pool of the current
+// device (created on first use; freed memory is kept for reuse).
+hipError_t workspace_alloc(void **p, size_t bytes, hipStream_t s);
+hipError_t workspace_free(void *p, hipStream_t s);
+
 // Blocked regime: inversion of all diagonal blocks of size nb (inner block ib).
 template <typename T>
 hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
