@@ -128,7 +128,9 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
 /*
  * Options for the *_ex entry points (a NULL opts means all defaults).
  *   nb    outer block size N_B of the blocked path (0: from the built-in
- *         table); must be a multiple of 16 in [16, 1024]
+ *         table); must be a multiple of 16 in [16, 2048]; above 1024 (above
+ *         512 for double complex) m must also be a multiple of nb, since
+ *         such blocks are inverted only by the blocked-inverse formula
  *   ib    inner block size I_B of the diagonal inversion (0: nb/8); must
  *         divide nb, and nb/ib <= 64
  *   path  HSMA_PATH_AUTO, HSMA_PATH_SMALL (requires m <= 64) or

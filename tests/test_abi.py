@@ -73,6 +73,11 @@ def test_ex_option_checks(hs):
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 128, "ib": 3}, 0) == hs.INVALID_VALUE
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 128, "ib": 1}, 0) == hs.INVALID_VALUE  # nb/ib > 64
     assert hs.entry("ex", "c128")(600, 4, 1, BAD, 600, BAD, 600, {"nb": 1024}, 0) == hs.INVALID_VALUE
+    # blocks above 1024 rows (512 for c128) need m to be a multiple of nb
+    assert f(3000, 4, 1, BAD, 3000, BAD, 3000, {"nb": 2048}, 0) == hs.INVALID_VALUE
+    assert f(3000, 4, 1, BAD, 3000, BAD, 3000, {"nb": 4096}, 0) == hs.INVALID_VALUE  # above 2048
+    assert hs.entry("ex", "c128")(3000, 4, 1, BAD, 3000, BAD, 3000, {"nb": 1024}, 0) == hs.INVALID_VALUE
+    assert hs.entry("diag_inv", "f32")(3000, 2048, 0, BAD, 3000, BAD, 0) == hs.INVALID_VALUE
 
 
 def test_solve_tri_checks(hs):
@@ -105,6 +110,7 @@ def test_block_size_table(hs):
         assert hs.hsma_trsm_block_size(code, 64) == 0
         for m in (65, 100, 1000, 1024, 3000, 8192, 16384, 50000):
             nb = hs.hsma_trsm_block_size(code, m)
-            assert nb % 16 == 0 and 16 <= nb <= 1024
+            assert nb % 16 == 0 and 16 <= nb <= 2048
             assert nb <= ((m + 15) // 16) * 16
+            assert nb <= (512 if code == 3 else 1024) or m % nb == 0
     assert hs.hsma_trsm_block_size(7, 100) == -1

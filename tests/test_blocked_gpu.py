@@ -157,6 +157,25 @@ def test_blocked_trsm(hs, dtype, m, n, nb):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("m,n,nb", [(2048, 100, 1024), (3000, 70, 1024), (4096, 64, 2048),
+                                    (2048, 33, 2048)])
+def test_blocked_trsm_large_blocks(hs, dtype, m, n, nb):
+    """N_B = 1024 / 2048: the blocked-inverse formula (m a multiple of N_B) and,
+    for m = 3000 with N_B = 1024 in the real and c64 types, the column
+    substitution kernel with its short last block; c128 above 512 and any
+    type above 1024 need m to be a multiple of N_B."""
+    if (nb > 1024 or dtype == "c128") and m % nb != 0:
+        pytest.skip("N_B above the column-substitution limit needs m % N_B == 0")
+    say("blocked large nb", dtype, m, n, nb)
+    A, B, X = blocked_solve(hs, dtype, m, n, nb, seed=m + n + nb)
+    Av, Bv = views(A, B, m)
+    Xo = oracle.trsm(Av, Bv)
+    Xg = X[:, :, :m].transpose(0, 2, 1)
+    assert rel_err(Xg, Xo) <= TOL_LARGE[dtype]
+    assert scaled_residual(np.ascontiguousarray(Av), Xg, Bv, 1.0) <= 10 * m * EPS[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_blocked_alpha_and_padding(hs, dtype):
     alpha = 0.3 + 0.7j if dtype.startswith("c") else -1.5
     say("blocked alpha", dtype)
@@ -168,22 +187,24 @@ def test_blocked_alpha_and_padding(hs, dtype):
 
 
 def test_blocked_exact_integer_all_nb(hs):
-    """Bidiagonal (1, -1) system with integer B: X = running sums exactly, for every N_B."""
+    """Bidiagonal (1, -1) system with integer B: X = running sums exactly, for every N_B
+    (m = 700: short last blocks; m = 4096 for the blocks above 512 rows)."""
     import torch
-    m, n = 700, 48
-    L = np.full((m, m), np.nan)
-    L[np.tril_indices(m, -1)] = 0
-    L[np.diag_indices(m)] = 1
-    L[np.arange(1, m), np.arange(m - 1)] = -1
+    n = 48
     rng = np.random.default_rng(1)
-    Bm = rng.integers(-30, 30, (m, n)).astype(np.float64)
-    for nb in (64, 128, 256, 512):
-        say("exact blocked", nb)
-        dA = to_dev(np.ascontiguousarray(L.T))
-        dB = to_dev(np.ascontiguousarray(Bm.T))
-        assert hs.hsma_trsm_ex_d(m, n, 1.0, dA, m, dB, m, {"nb": nb, "path": 2}) == hs.SUCCESS
-        torch.cuda.synchronize()
-        assert np.array_equal(dB.cpu().numpy().T, np.cumsum(Bm, axis=0))
+    for m, nbs in ((700, (64, 128, 256, 512)), (4096, (1024, 2048))):
+        L = np.full((m, m), np.nan)
+        L[np.tril_indices(m, -1)] = 0
+        L[np.diag_indices(m)] = 1
+        L[np.arange(1, m), np.arange(m - 1)] = -1
+        Bm = rng.integers(-30, 30, (m, n)).astype(np.float64)
+        for nb in nbs:
+            say("exact blocked", m, nb)
+            dA = to_dev(np.ascontiguousarray(L.T))
+            dB = to_dev(np.ascontiguousarray(Bm.T))
+            assert hs.hsma_trsm_ex_d(m, n, 1.0, dA, m, dB, m, {"nb": nb, "path": 2}) == hs.SUCCESS
+            torch.cuda.synchronize()
+            assert np.array_equal(dB.cpu().numpy().T, np.cumsum(Bm, axis=0))
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -104,7 +104,18 @@ int table_lookup(int dtype, int64_t m)
     return tab[best].nb;
 }
 
-bool valid_nb(int64_t nb) { return nb >= 16 && nb <= 1024 && nb % 16 == 0; }
+constexpr int kMaxNb = 2048;
+
+bool valid_nb(int64_t nb) { return nb >= 16 && nb <= kMaxNb && nb % 16 == 0; }
+
+// Large blocks are inverted only by the blocked-inverse formula, which needs
+// m to be a multiple of N_B: above 1024 rows (the column-substitution kernel
+// holds at most 1024 rows of an identity tile in registers), and above 512
+// for double complex.
+bool nb_fits(int64_t nb, int64_t m, int dtype)
+{
+    return nb <= (dtype == 3 ? 512 : 1024) || m % nb == 0;
+}
 
 int env_nb()
 {
@@ -121,13 +132,13 @@ int env_nb()
     return value;
 }
 
-int max_nb_for(int dtype) { return dtype == 3 ? 512 : 1024; }
 
 int choose_nb(int dtype, int64_t m)
 {
     int nb = env_nb();
     if (nb <= 0) nb = table_lookup(dtype, m);
-    if (nb > max_nb_for(dtype)) nb = max_nb_for(dtype);
+    if (nb > kMaxNb) nb = kMaxNb;
+    while (!nb_fits(nb, m, dtype)) nb /= 2;
     const int64_t cap = ((m + 15) / 16) * 16;
     if (nb > cap) nb = (int)(cap < 16 ? 16 : cap);
     return nb;
@@ -152,7 +163,7 @@ hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
     if (!o) return HSMA_STATUS_SUCCESS;
     if (o->path < HSMA_PATH_AUTO || o->path > HSMA_PATH_BLOCKED) return HSMA_STATUS_INVALID_VALUE;
     if (o->path == HSMA_PATH_SMALL && m > 64) return HSMA_STATUS_INVALID_VALUE;
-    if (o->nb != 0 && (!valid_nb(o->nb) || o->nb > max_nb_for(dtype)))
+    if (o->nb != 0 && (!valid_nb(o->nb) || !nb_fits(o->nb, m, dtype)))
         return HSMA_STATUS_INVALID_VALUE;
     if (o->ib != 0) {
         const int nb = o->nb != 0 ? o->nb : 0;
@@ -232,7 +243,7 @@ hsma_status diag_inv_impl(int64_t m, int32_t nb, int32_t ib, const T *A, int64_t
     constexpr int dt = traits<T>::dtype;
     if (m < 0 || lda < imax(1, m)) return HSMA_STATUS_INVALID_SIZE;
     if (nb == 0) nb = choose_nb(dt, m > 64 ? m : 65);
-    if (!valid_nb(nb) || nb > max_nb_for(dt)) return HSMA_STATUS_INVALID_VALUE;
+    if (!valid_nb(nb) || !nb_fits(nb, m, dt)) return HSMA_STATUS_INVALID_VALUE;
     if (ib == 0) ib = nb / 8;
     if (ib < 1 || nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
     if (m == 0) return HSMA_STATUS_SUCCESS;

@@ -135,6 +135,7 @@ static hipError_t diag_inv_launch(int64_t m, int nb, const T *A, int64_t lda, T 
 {
     const int64_t nt = (m + nb - 1) / nb;
     if (nt > 65535) return hipErrorInvalidConfiguration;
+    if (nb > 1024) return hipErrorInvalidValue;  // 256 threads x at most 4 rows
     const dim3 grid((unsigned)((nb + G - 1) / G), (unsigned)nt);
     if (nb <= 256)
         hipLaunchKernelGGL((diag_inv_kernel<T, 1, G>), grid, dim3(256), 0, s, A, lda, m, nb, invA);
@@ -236,6 +237,8 @@ template <> struct vec16<float> { using type = f32x4; static constexpr int N = 4
 template <> struct vec16<double> { using type = f64x2; static constexpr int N = 2; };
 
 constexpr int kBM = 128, kBN = 128;
+constexpr int kXcds = 8;        // XCDs of the GPU (round-robin workgroup placement)
+constexpr int64_t kGroupRows = 8;  // row tiles per group in the XCD-local tile order
 
 // Real view of the product: Mr x N output from an Mr x Kr "A" and a Kr x N
 // "B". For complex T, Mr = 2M, Kr = 2K, and B, C are the complex arrays read
@@ -283,8 +286,26 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
     const int wave = tid >> 6;
     const int wi = (wave & 1) * 64;   // wave's row offset inside the tile (i)
     const int wj = (wave >> 1) * 64;  // wave's column offset (j)
-    int64_t i0 = (int64_t)blockIdx.x * kBM;  // row tile; reassigned per paired tile below
-    const int64_t j0 = (int64_t)blockIdx.y * kBN;
+    // Tile of this workgroup. Workgroups are dealt to the 8 XCDs round-robin
+    // by linear id, and each XCD has its own L2; for a single product the
+    // ids are renumbered so that every XCD gets a contiguous range, walked in
+    // groups of kGroupRows row tiles, so the workgroups resident on one XCD
+    // share a few A row panels and B column panels.
+    int64_t bx = blockIdx.x, by = blockIdx.y;
+    if constexpr (!PAIR) {
+        const int64_t gx = gridDim.x, gy = gridDim.y, total = gx * gy;
+        if (gridDim.z == 1 && total % kXcds == 0) {
+            const int64_t id = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gx;
+            const int64_t t = (id % kXcds) * (total / kXcds) + id / kXcds;
+            const int64_t first = t / (kGroupRows * gy) * kGroupRows;
+            const int64_t gs = gx - first < kGroupRows ? gx - first : kGroupRows;
+            const int64_t r = t % (kGroupRows * gy);
+            bx = first + r % gs;
+            by = r / gs;
+        }
+    }
+    int64_t i0 = bx * kBM;  // row tile; reassigned per paired tile below
+    const int64_t j0 = by * kBN;
     {
         const int64_t z = blockIdx.z, g = z / p.bin, k = z % p.bin;
         p.A += g * p.sAo + k * p.sAi;
@@ -421,10 +442,10 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
     };
 
     const int64_t ntile_rows = (p.Mr + kBM - 1) / kBM;
-    const int nrep = (PAIR && 2 * (int64_t)blockIdx.x + 1 != ntile_rows) ? 2 : 1;
+    const int nrep = (PAIR && 2 * bx + 1 != ntile_rows) ? 2 : 1;
     for (int rep = 0; rep < (PAIR ? 2 : 1); ++rep) {
     if (rep >= nrep) break;
-    i0 = (rep == 0 ? (int64_t)blockIdx.x : ntile_rows - 1 - (int64_t)blockIdx.x) * kBM;
+    i0 = (rep == 0 ? bx : ntile_rows - 1 - bx) * kBM;
     kend = p.Kr;
     if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
     tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;

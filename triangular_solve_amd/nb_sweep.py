@@ -18,7 +18,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DTYPES = ["f32", "f64", "c64", "c128"]
-CANDIDATES = [64, 128, 256, 512, 1024]
+CANDIDATES = [64, 128, 256, 512, 1024, 2048]
 
 
 def sweep(sizes, dtypes, reps, n=None, log=print):
@@ -38,7 +38,7 @@ def sweep(sizes, dtypes, reps, n=None, log=print):
             B = B0.clone()
             best = None
             for nb in CANDIDATES:
-                if nb > 2 * m or (dt == "c128" and nb > 512):
+                if nb > 2 * m or (nb > (512 if dt == "c128" else 1024) and m % nb != 0):
                     continue
                 times = []
                 for r in range(reps + 1):
