@@ -169,13 +169,16 @@ def test_solve_tri_ggml_shapes(hs):
         assert nmse <= 1e-7    # the test-backend-ops gate on the SOLVE_TRI page
 
 
-def test_solve_tri_strided_views(hs):
+# n = 48: rows staged through LDS; n = 64 with 16-byte aligned row strides:
+# rows of A kept in registers; n = 64 with odd strides: back to LDS staging
+@pytest.mark.parametrize("n,sA1,pa2,pa3", [(48, 50, 5, 7), (64, 68, 4, 8), (64, 65, 5, 7)])
+def test_solve_tri_strided_views(hs, n, sA1, pa2, pa3):
     """Non-contiguous batches: A, B, X inside larger buffers with padded strides."""
     import torch
-    n, k, e2, e3 = 48, 7, 3, 2
-    sA1, sB1, sX1 = 50, 9, 11
-    sA2, sB2, sX2 = n * sA1 + 5, n * sB1 + 3, n * sX1 + 2
-    sA3, sB3, sX3 = e2 * sA2 + 7, e2 * sB2 + 1, e2 * sX2 + 4
+    k, e2, e3 = 7, 3, 2
+    sB1, sX1 = 9, 11
+    sA2, sB2, sX2 = n * sA1 + pa2, n * sB1 + 3, n * sX1 + 2
+    sA3, sB3, sX3 = e2 * sA2 + pa3, e2 * sB2 + 1, e2 * sX2 + 4
     rng = np.random.default_rng(3)
     Abuf = rng.standard_normal(e3 * sA3).astype(np.float32)
     Bbuf = rng.standard_normal(e3 * sB3).astype(np.float32)

@@ -51,10 +51,14 @@ struct RowlaneArgs {
 
 constexpr int kLdsStride = 65;  // padded LDS column stride of the staged triangle
 
-template <typename T, int KW>
+// RR: lane i keeps row i of A in registers, loaded with 16-byte loads (real
+// types, m = 64, rows contiguous and 16-byte aligned: the ggml row-major
+// layout). Then nothing is staged in LDS and no barrier is needed; step j
+// reads its coefficient a_ij from register j.
+template <typename T, int KW, bool RR>
 __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
 {
-    __shared__ T AT[64 * kLdsStride];
+    __shared__ T AT[RR ? 1 : 64 * kLdsStride];
 
     const int64_t b = blockIdx.x;
     const int64_t i2 = b % p.ne02, i3 = b / p.ne02;
@@ -70,6 +74,40 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
     if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
     // Lane i owns row i: its own 1/a_ii, no exchange needed.
     const T inv = recip(lane < m ? Ab[lane * (p.sai + p.saj)] : one);
+
+    if constexpr (RR) {
+        static_assert(!traits<T>::is_complex, "row registers for real types only");
+        constexpr int V = 16 / (int)sizeof(T);
+        typedef T vec_t __attribute__((ext_vector_type(V)));
+        // a[j] = a_ij / a_ii below the diagonal, 0 on and above it
+        T a[64];
+        const T *Ar = Ab + lane * p.sai;
+#pragma unroll
+        for (int k = 0; k < 64 / V; ++k) {
+            const vec_t v = *(const vec_t *)(Ar + k * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e) a[k * V + e] = v[e];
+        }
+        const int c0 = (blockIdx.y * nw + wave) * KW;
+        T w[KW];
+#pragma unroll
+        for (int q = 0; q < KW; ++q) {
+            const int c = c0 + q;
+            w[q] = c < p.n ? mul(mul(p.alpha, Bb[lane * p.sbi + c * p.sbj]), inv) : zero_of(T());
+        }
+#pragma unroll
+        for (int j = 0; j < 64; ++j) a[j] = j < lane ? mul(a[j], inv) : zero_of(T());
+#pragma unroll
+        for (int j = 0; j < 64; ++j)
+#pragma unroll
+            for (int q = 0; q < KW; ++q) w[q] = fms(w[q], a[j], readlane(w[q], j));
+#pragma unroll
+        for (int q = 0; q < KW; ++q) {
+            const int c = c0 + q;
+            if (c < p.n) Xb[lane * p.sxi + c * p.sxj] = w[q];
+        }
+        return;
+    }
 
     // Stage tril(A) scaled by its row's inverse diagonal, strictly lower part
     // only (diagonal and above are zero), transposed: AT[j][i] = a_ij / a_ii.
@@ -131,8 +169,20 @@ static hipError_t rowlane_launch(const RowlaneArgs<T> &p, int64_t nprob, int nwa
     const int64_t ychunks = (p.n + per_block - 1) / per_block;
     if (ychunks > 65535) return hipErrorInvalidConfiguration;
     if (nprob > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rowlane_kernel<T, KW>), dim3((unsigned)nprob, (unsigned)ychunks),
-                       dim3(64 * nwaves), 0, s, p);
+    const dim3 grid((unsigned)nprob, (unsigned)ychunks);
+    // Rows in registers: m = 64, contiguous 16-byte aligned rows of A (all
+    // problems), real types with few columns per wave.
+    const int64_t sz = (int64_t)sizeof(T);
+    const bool rr = !traits<T>::is_complex && KW <= 4 && p.m == 64 && p.saj == 1 &&
+                    (uintptr_t)p.A % 16 == 0 && (p.sai * sz) % 16 == 0 &&
+                    (p.sa2 * sz) % 16 == 0 && (p.sa3 * sz) % 16 == 0;
+    if constexpr (!traits<T>::is_complex && KW <= 4) {
+        if (rr) {
+            hipLaunchKernelGGL((rowlane_kernel<T, KW, true>), grid, dim3(64 * nwaves), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((rowlane_kernel<T, KW, false>), grid, dim3(64 * nwaves), 0, s, p);
     return hipGetLastError();
 }
 
