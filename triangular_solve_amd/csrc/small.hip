@@ -419,7 +419,6 @@ struct PanelState {
     T x;          // multiplier of the current column segment
     cptr<T> a4;   // A of this problem (scalar loads)
     int64_t lda;
-    T *Bc;        // this lane's column of B (read back finished rows)
     T *Bw;        // first of the wave's 64 columns of B
     int64_t ldb;
     int ncol;     // columns of the wave that exist (<= 64)
@@ -508,6 +507,44 @@ __device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, in
     }
 }
 
+// Rows [k0, k0 + 8) of the wave's columns of B (one 128-byte line per
+// column, double complex: the only type with a second row panel) into the
+// tile: the finished x of the first panel, read back by the reload
+// segments. The lines go straight from memory into LDS (no registers):
+// instruction q fetches the lines of columns 8q..8q+7 and lane 8a+b lands at
+// byte 16(8a+b) of the instruction's 1 KB; the lane fetches row (a+b) mod 8
+// of column 8q+b, so that reload_x's eight lanes of a group of columns
+// read eight different 16-byte bank groups.
+template <typename T, int P>
+__device__ __forceinline__ void reload_fill(PanelState<T, P> &st, int k0)
+{
+    static_assert(sizeof(T) == 16, "one element per 16 bytes");
+    const int lane = threadIdx.x & 63;
+    const int a = lane >> 3, b = lane & 7;
+    const int r = (a + b) & 7;
+    const gptr<T> bw = global_after(st.Bw, st.x);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        int col = q * 8 + b;
+        col = col < st.ncol ? col : st.ncol - 1;  // duplicates of a valid column
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(bw + (col * st.ldb + k0 + r)),
+                                         (__attribute__((address_space(3))) void *)(st.tile + q * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
+}
+
+// x of row k0 + k (k < 8) of this lane's column from the tile reload_fill wrote.
+template <typename T, int P>
+__device__ __forceinline__ T reload_x(const PanelState<T, P> &st, int k)
+{
+    const int c = threadIdx.x & 63;
+    const int q = c >> 3, b = c & 7;
+    using R = typename traits<T>::real;
+    const __attribute__((address_space(3))) R *e =
+        (const __attribute__((address_space(3))) R *)(st.tile + q * 1024 + (8 * ((k - b) & 7) + b) * 16);
+    return T{e[0], e[1]};
+}
+
 // Scalar loads of the pieces [Q, Q1) of a batch into cb.
 template <typename T, int P, int R0, int G, int Q, int Q1>
 __device__ __forceinline__ void batch_load(T (&cb)[G], cptr<T> ap, int64_t lda)
@@ -533,9 +570,11 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
         constexpr int off = Plan::T.off[Q];
         if constexpr (pc.first) {
             if constexpr (pc.reload) {
-                // finished x_k of an earlier panel, read back from B
-                const gptr<T> bk = global_after(st.Bc + pc.col, st.x);
-                st.x = mul(ld_global<T>(bk, 0), st.alpha_inv);
+                // finished x_k of an earlier panel, read back from B through
+                // the tile: one line of rows per refill for all the wave's
+                // columns, then one LDS read per segment
+                if constexpr (pc.col % 8 == 0) reload_fill<T, P>(st, pc.col);
+                st.x = mul(reload_x<T, P>(st, pc.col % 8), st.alpha_inv);
             } else {
                 constexpr int j = pc.col - R0;
                 // Tie the broadcast of 1/a_jj to w[j] so the compiler cannot
@@ -646,8 +685,6 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     if (item >= items) return;  // whole wave leaves together; no barriers below
     const int64_t prob = item / nchunks;
     const int64_t cfirst = (item % nchunks) * 64;
-    const int64_t c = cfirst + lane;
-    const bool live = c < n;
 
     // problem prob = g * per + k lives at A + g*strideA2 + k*strideA (B alike)
     const int64_t pg = prob / per, pk = prob % per;
@@ -659,7 +696,6 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     PanelState<T, P> st;
     st.a4 = (cptr<T>)Ap;
     st.lda = lda;
-    st.Bc = Bc0 + (live ? lane : 0) * ldb;
     st.Bw = Bc0;
     st.ldb = ldb;
     st.ncol = (int)(n - cfirst < 64 ? n - cfirst : 64);
