@@ -29,6 +29,8 @@
 //    substitution, any m <= 64, any strides (column-major or the row-major
 //    ggml layout), in place or out of place. This is the latency kernel for
 //    few right-hand sides (the SOLVE_TRI shape) and the general fallback.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -295,18 +297,22 @@ __device__ __forceinline__ void order_after(V &v, const T &dep)
 // most G coefficients. A batch is fetched with scalar loads and consumed
 // after a single wait: scalar loads can return out of order, so every wait
 // is a full wait, and fewer, larger batches mean fewer exposed latencies.
-template <int P, int R0, int G>
+// DIAG: an own column's segment starts at its diagonal entry, so the batch
+// also brings a_jj and x_j = w_j / a_jj is formed from it.
+template <int P, int R0, int G, bool DIAG>
 struct PanelPlan {
     struct Piece {
         int col, lo, hi;  // column of A, panel-local rows [lo, hi)
         int first;        // first piece of its segment: x is formed here
         int reload;       // segment of an earlier panel: x is read back
+        int diag;         // row lo is the diagonal entry a_jj
     };
     static constexpr int count()
     {
         int n = 0;
         for (int k = 0; k < R0; ++k) n += (P + G - 1) / G;
-        for (int j = 0; j < P; ++j) n += (P - 1 - j) == 0 ? 1 : (P - 1 - j + G - 1) / G;
+        for (int j = 0; j < P; ++j)
+            n += DIAG ? (P - j + G - 1) / G : (P - 1 - j) == 0 ? 1 : (P - 1 - j + G - 1) / G;
         return n;
     }
     static constexpr int NP = count();
@@ -322,11 +328,16 @@ struct PanelPlan {
         int n = 0;
         for (int k = 0; k < R0; ++k)
             for (int lo = 0; lo < P; lo += G)
-                t.pc[n++] = Piece{k, lo, lo + G < P ? lo + G : P, lo == 0, 1};
+                t.pc[n++] = Piece{k, lo, lo + G < P ? lo + G : P, lo == 0, 1, 0};
         for (int j = 0; j < P; ++j) {
-            if (j + 1 == P) { t.pc[n++] = Piece{R0 + j, P, P, 1, 0}; continue; }
+            if (DIAG) {
+                for (int lo = j; lo < P; lo += G)
+                    t.pc[n++] = Piece{R0 + j, lo, lo + G < P ? lo + G : P, lo == j, 0, lo == j};
+                continue;
+            }
+            if (j + 1 == P) { t.pc[n++] = Piece{R0 + j, P, P, 1, 0, 0}; continue; }
             for (int lo = j + 1; lo < P; lo += G)
-                t.pc[n++] = Piece{R0 + j, lo, lo + G < P ? lo + G : P, lo == j + 1, 0};
+                t.pc[n++] = Piece{R0 + j, lo, lo + G < P ? lo + G : P, lo == j + 1, 0, 0};
         }
         int b = 0, used = 0;
         t.bfirst[0] = 0;
@@ -342,6 +353,13 @@ struct PanelPlan {
     }
     static constexpr Table T = build();
 };
+
+// The diagonal travels with the coefficient stream for f32, whose
+// reciprocal is one v_rcp_f32 on the scalar value (within an ulp). For the
+// other types a full-precision reciprocal per column would cost several
+// instructions, so every lane computes 1/a_ll of its row once at the start.
+template <typename T>
+constexpr bool kDiagInStream = std::is_same<T, float>::value;
 
 // Coefficients per batch: 64 dwords of SGPRs.
 template <typename T>
@@ -362,10 +380,10 @@ constexpr int kAhead = sizeof(T) == 16 ? 48 : 96;
 // scalar loads. The scalar loads then find the lines in L2 instead of
 // waiting on HBM with a full wait each. Both tb and cb grow with s, so each
 // batch handles a contiguous range of segments.
-template <int P, int R0, int G, int AH>
+template <int P, int R0, int G, int AH, bool DIAG>
 struct TouchPlan {
-    using Plan = PanelPlan<P, R0, G>;
-    static constexpr int NS = R0 + P - 1;
+    using Plan = PanelPlan<P, R0, G, DIAG>;
+    static constexpr int NS = R0 + P - (DIAG ? 0 : 1);
     struct Seg {
         int col, lo, hi;
     };
@@ -550,7 +568,7 @@ template <typename T, int P, int R0, int G, int Q, int Q1>
 __device__ __forceinline__ void batch_load(T (&cb)[G], cptr<T> ap, int64_t lda)
 {
     if constexpr (Q < Q1) {
-        using Plan = PanelPlan<P, R0, G>;
+        using Plan = PanelPlan<P, R0, G, kDiagInStream<T>>;
         constexpr auto pc = Plan::T.pc[Q];
         constexpr int off = Plan::T.off[Q];
         const cptr<T> colp = ap + (R0 + (int64_t)pc.col * lda);
@@ -565,7 +583,7 @@ template <typename T, int P, int R0, int G, int Q, int Q1>
 __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb)[G])
 {
     if constexpr (Q < Q1) {
-        using Plan = PanelPlan<P, R0, G>;
+        using Plan = PanelPlan<P, R0, G, kDiagInStream<T>>;
         constexpr auto pc = Plan::T.pc[Q];
         constexpr int off = Plan::T.off[Q];
         if constexpr (pc.first) {
@@ -575,6 +593,14 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
                 // columns, then one LDS read per segment
                 if constexpr (pc.col % 8 == 0) reload_fill<T, P>(st, pc.col);
                 st.x = mul(reload_x<T, P>(st, pc.col % 8), st.alpha_inv);
+            } else if constexpr (pc.diag) {
+                constexpr int j = pc.col - R0;
+                if constexpr (std::is_same<T, float>::value) {
+                    float r = __builtin_amdgcn_rcpf(cb[off]);
+                    asm volatile("" : "+v"(r) : "v"(st.w[j]));
+                    st.x = st.w[j] * r;
+                }
+                st.w[j] = st.x;
             } else {
                 constexpr int j = pc.col - R0;
                 // Tie the broadcast of 1/a_jj to w[j] so the compiler cannot
@@ -590,7 +616,7 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
             }
         }
 #pragma unroll
-        for (int r = pc.lo; r < pc.hi; ++r) st.w[r] = fms(st.w[r], cb[off + r - pc.lo], st.x);
+        for (int r = pc.lo + pc.diag; r < pc.hi; ++r) st.w[r] = fms(st.w[r], cb[off + r - pc.lo], st.x);
         batch_compute<T, P, R0, G, Q + 1, Q1>(st, cb);
     }
 }
@@ -603,7 +629,7 @@ template <typename T, int P, int R0, int G, int AH, int S, int S1>
 __device__ __forceinline__ void batch_touch(PanelState<T, P> &st, cptr<T> ap)
 {
     if constexpr (S < S1) {
-        constexpr auto sg = TouchPlan<P, R0, G, AH>::T.sg[S];
+        constexpr auto sg = TouchPlan<P, R0, G, AH, kDiagInStream<T>>::T.sg[S];
         const uint64_t first = (uint64_t)(ap + (R0 + sg.lo + (int64_t)sg.col * st.lda));
         const uint64_t line = first & ~(uint64_t)127;
         const int bytes = (int)(first - line) + (sg.hi - sg.lo) * (int)sizeof(T);
@@ -629,8 +655,8 @@ __device__ __forceinline__ void batch_retire(PanelState<T, P> &st)
 template <typename T, int P, int R0, int G, int AH, int Bi>
 __device__ __forceinline__ void run_batches(PanelState<T, P> &st)
 {
-    using Plan = PanelPlan<P, R0, G>;
-    using TP = TouchPlan<P, R0, G, AH>;
+    using Plan = PanelPlan<P, R0, G, kDiagInStream<T>>;
+    using TP = TouchPlan<P, R0, G, AH, kDiagInStream<T>>;
     if constexpr (Bi < Plan::T.nbatch) {
         constexpr int p0 = Plan::T.bfirst[Bi], p1 = Plan::T.bfirst[Bi + 1];
         // fetch this batch once the previous one has been consumed
@@ -703,7 +729,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     st.alpha_inv = alpha_inv;
 
     st.lane128 = lane * 128;
-    st.myinv = recip(Ap[lane + lane * lda]);
+    if constexpr (!kDiagInStream<T>) st.myinv = recip(Ap[lane + lane * lda]);
     run_panels<T, P, NPANEL, 0>(st, alpha, typename traits<T>::real(0));
 }
 
