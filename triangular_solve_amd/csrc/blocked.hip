@@ -658,11 +658,15 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
                             invA, nb, 2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, R(0), temp, sz,
                             sz * sz, pairs * sz * sz, pairs, batch, false, s);
         if (e != hipSuccess) return e;
-        // inv21 = -inv22 * T
+        // inv21 = -inv22 * T. inv22 is lower triangular with exact zeros above
+        // its diagonal, so it is multiplied as a full matrix: the zero tiles
+        // add exact zeros, and the full product keeps all its tiles in
+        // flight (the triangular form pairs row tiles and halves the
+        // workgroups, which leaves CUs idle at these batch sizes).
         e = gemm_batched<T>(sz, sz, sz, R(-1), invA + sz * ((int64_t)nb + 1), nb,
                             2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, temp, sz, sz * sz,
                             pairs * sz * sz, R(0), invA + sz, nb, 2 * sz * ((int64_t)nb + 1),
-                            (int64_t)nb * nb, pairs, batch, true, s);
+                            (int64_t)nb * nb, pairs, batch, false, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
