@@ -147,13 +147,14 @@ def bench_batched(hs, torch, steps, warmup, m=64, n=64, batch=4096, check=True):
             "wall_s": wall, "host": host}
 
 
-def bench_solve_tri(hs, torch, runs=2000):
-    """The SOLVE_TRI shape of the llama.cpp PR: A [64,64,4,2], B [6,64,4,2], f32."""
+def bench_solve_tri(hs, torch, runs=2000, n=64, k=6, e2=4, e3=2):
+    """A SOLVE_TRI shape of the llama.cpp PR, f32, ggml layout: by default its
+    performance shape A [64,64,4,2], B [6,64,4,2]; with n = 128, k = 8, e2 = 4,
+    e3 = 1 the [128,128,4,1] case its kernel reports as not supported."""
     import oracle
     import synth
-    n, k, e2, e3 = 64, 6, 4, 2
     nb = e2 * e3
-    A = synth.tri("f32", n, nb, seed=SEED_CFG0, offdiag_div=64, layout="row")
+    A = synth.tri("f32", n, nb, seed=SEED_CFG0, offdiag_div=n, layout="row")
     B = synth.rhs("f32", n, k, nb, seed=SEED_CFG0 + 1, layout="row")
     dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
     dX = torch.empty_like(dB)
@@ -179,7 +180,7 @@ def bench_solve_tri(hs, torch, runs=2000):
         samples.append(a.elapsed_time(b) * 1e3 / (runs // 10))
     us = float(np.mean(samples[1:]))
     nbytes = ggml_bytes(n, k, nb, 4)
-    return {"shape": "A[64,64,4,2] B[6,64,4,2] f32 (ggml layout, out of place)",
+    return {"shape": "A[%d,%d,%d,%d] B[%d,%d,%d,%d] f32 (ggml layout, out of place)" % (n, n, e2, e3, k, n, e2, e3),
             "us_per_call": us, "ggml_kB_per_run": nbytes / 1024, "ggml_GiB_per_s": nbytes / (us * 1e-6) / 2 ** 30,
             "gflops": lapack_flops("f32", n, k) * nb / (us * 1e-6) / 1e9, "rel_err": err, "nmse": nmse,
             "launches_timed": runs}
@@ -348,6 +349,8 @@ def main():
     dom = max(per, key=lambda d: per[d]["ms_per_launch"])
     log("solve_tri shape")
     st = bench_solve_tri(hs, torch)
+    log("solve_tri 128 shape")
+    st128 = bench_solve_tri(hs, torch, runs=1000, n=128, k=8, e2=4, e3=1)
     blocked = None
     if not args.no_blocked:
         blocked = bench_blocked(hs, torch, 8192, DTYPES, runs=3)
@@ -364,7 +367,7 @@ def main():
                      "kernel": "colane_kernel (%s), %d algorithmic bytes per launch" % (dom, per[dom]["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "per_dtype": per,
-        "solve_tri": st,
+        "solve_tri": st, "solve_tri_128": st128,
         "blocked_8192": blocked,
     }
     print(json.dumps(line), flush=True)

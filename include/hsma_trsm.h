@@ -117,8 +117,11 @@ hsma_status hsma_trsm_strided_batched_z(int64_t m, int64_t n, hsma_double_comple
  *   X(i, c) = X[i*sX1 + c + i2*sX2 + i3*sX3]
  * Strides are in elements (floats), as the PR's reviewers asked. B is
  * read-only; X must not overlap A or B.
- * n <= 64 (any k); larger n returns NOT_SUPPORTED, as the PR's kernel
- * reports for the [128,128,4,1] case.
+ * n <= 256 (any k). For n <= 64 one launch solves every batch entry on
+ * chip; for 64 < n <= 256 (the [128,128,4,1] case the PR's kernel reports
+ * as not supported) the rows are solved in blocks of 64, two launches per
+ * block row, with the finished rows of X read back for the next block.
+ * n > 256 returns NOT_SUPPORTED.
  */
 hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float *B, float *X,
                                int64_t ne02, int64_t ne03, int64_t sA1, int64_t sA2, int64_t sA3,

@@ -82,9 +82,13 @@ def test_ex_option_checks(hs):
 
 def test_solve_tri_checks(hs):
     f = hs.hsma_solve_tri_f32
-    # the PR's [128,128,4,1] / [8,128,4,1] case is not supported by this entry
-    assert f(128, 8, BAD, BAD, BAD, 4, 1, 128, 128 * 128, 4 * 128 * 128, 8, 8 * 128, 4 * 8 * 128,
-             8, 8 * 128, 4 * 8 * 128, 0) == hs.NOT_SUPPORTED
+    # n <= 256 is handled (in blocks of 64 above 64); larger n is not supported
+    assert f(257, 8, BAD, BAD, BAD, 4, 1, 257, 257 * 257, 4 * 257 * 257, 8, 8 * 257, 4 * 8 * 257,
+             8, 8 * 257, 4 * 8 * 257, 0) == hs.NOT_SUPPORTED
+    assert f(128, 8, BAD, BAD, BAD, 4, 1, 127, 128 * 128, 4 * 128 * 128, 8, 8 * 128, 4 * 8 * 128,
+             8, 8 * 128, 4 * 8 * 128, 0) == hs.INVALID_SIZE    # row stride below n
+    assert f(128, 8, BAD, None, BAD, 4, 1, 128, 128 * 128, 4 * 128 * 128, 8, 8 * 128, 4 * 8 * 128,
+             8, 8 * 128, 4 * 8 * 128, 0) == hs.INVALID_POINTER
     assert f(64, 6, BAD, BAD, BAD, 4, 2, 63, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.INVALID_SIZE
     assert f(64, 6, BAD, None, BAD, 4, 2, 64, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.INVALID_POINTER
     assert f(64, 0, None, None, None, 4, 2, 64, 4096, 16384, 6, 384, 1536, 6, 384, 1536, 0) == hs.SUCCESS

@@ -169,9 +169,23 @@ def test_solve_tri_ggml_shapes(hs):
         assert nmse <= 1e-7    # the test-backend-ops gate on the SOLVE_TRI page
 
 
+def test_solve_tri_medium_sizes(hs):
+    """64 < n <= 256: block rows of 64 (the PR's [128,128,4,1] / [8,128,4,1]
+    case included), ragged last blocks, k above and below the 8-column
+    update groups."""
+    for (n, k, e2, e3) in [(128, 8, 4, 1), (100, 5, 2, 3), (65, 1, 1, 1), (256, 6, 1, 2),
+                           (200, 130, 1, 1), (192, 64, 2, 1)]:
+        say("solve_tri medium", n, k, e2, e3)
+        X, Xo, A, B = ggml_case(hs, n, k, e2, e3, seed=n + 3 * k)
+        assert rel_err(X, Xo) <= TOL_SMALL["f32"]
+        nmse = float(np.sum((X - Xo) ** 2) / np.sum(Xo ** 2))
+        assert nmse <= 1e-7
+
+
 # n = 48: rows staged through LDS; n = 64 with 16-byte aligned row strides:
 # rows of A kept in registers; n = 64 with odd strides: back to LDS staging
-@pytest.mark.parametrize("n,sA1,pa2,pa3", [(48, 50, 5, 7), (64, 68, 4, 8), (64, 65, 5, 7)])
+@pytest.mark.parametrize("n,sA1,pa2,pa3", [(48, 50, 5, 7), (64, 68, 4, 8), (64, 65, 5, 7),
+                                           (150, 152, 4, 8), (130, 131, 5, 7)])
 def test_solve_tri_strided_views(hs, n, sA1, pa2, pa3):
     """Non-contiguous batches: A, B, X inside larger buffers with padded strides."""
     import torch

@@ -105,6 +105,7 @@ int table_lookup(int dtype, int64_t m)
 }
 
 constexpr int kMaxNb = 2048;
+constexpr int64_t kSolveTriMaxN = 256;  // SOLVE_TRI sizes handled (block rows of 64 above 64)
 
 bool valid_nb(int64_t nb) { return nb >= 16 && nb <= kMaxNb && nb % 16 == 0; }
 
@@ -369,11 +370,14 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
     try {
         if (n < 0 || k < 0 || ne02 < 0 || ne03 < 0) return HSMA_STATUS_INVALID_SIZE;
         if (n == 0 || k == 0 || ne02 == 0 || ne03 == 0) return HSMA_STATUS_SUCCESS;
-        if (n > 64) return HSMA_STATUS_NOT_SUPPORTED;
+        if (n > kSolveTriMaxN) return HSMA_STATUS_NOT_SUPPORTED;
         if (sA1 < n || sB1 < k || sX1 < k) return HSMA_STATUS_INVALID_SIZE;
         if (sA2 < 0 || sA3 < 0 || sB2 < 0 || sB3 < 0 || sX2 < 0 || sX3 < 0)
             return HSMA_STATUS_INVALID_SIZE;
         if (!A || !B || !X) return HSMA_STATUS_INVALID_POINTER;
+        if (n > 64)
+            return hip_status(solve_tri_medium(n, k, A, B, X, ne02, ne03, sA1, sA2, sA3, sB1, sB2,
+                                               sB3, sX1, sX2, sX3, (hipStream_t)stream));
         return hip_status(small_rowlane<float>(A, sA1, 1, sA2, sA3, B, sB1, 1, sB2, sB3, X, sX1, 1,
                                                sX2, sX3, n, k, ne02, ne03, 1.0f,
                                                (hipStream_t)stream));
