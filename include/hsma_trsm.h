@@ -89,7 +89,10 @@ hsma_status hsma_trsm_z(int64_t m, int64_t n, hsma_double_complex alpha,
  * strideA == 0 shares one A across the batch. B blocks must not overlap:
  * strideB >= ldb*n when batch_count > 1 (else INVALID_SIZE).
  * m <= 64 runs as one launch over the whole batch (the pages' small regime);
- * larger m runs the blocked solver once per problem.
+ * 64 < m <= 256 runs in block rows of 64 over the whole batch (per block row
+ * one batched GEMM update with the finished rows and one batched small-regime
+ * solve of the diagonal blocks); larger m runs the blocked solver once per
+ * problem.
  */
 hsma_status hsma_trsm_strided_batched_s(int64_t m, int64_t n, float alpha, const float *A,
                                         int64_t lda, int64_t strideA, float *B, int64_t ldb,

@@ -191,6 +191,38 @@ hipError_t small_path(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
                             m, n, batch, 1, alpha, s);
 }
 
+// Batches of 64 < m <= 256: block rows of 64 for the whole batch at once
+// (X_r = A_rr^{-1} (B_r - A[r, <r] X_<r)), the update by one strided-batched
+// matrix-core GEMM and the diagonal solve by the small regime, both over all
+// problems; 2 * ceil(m/64) launches instead of a blocked solve per problem.
+constexpr int64_t kMediumMaxM = 256;
+
+template <typename T>
+hipError_t medium_batched(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
+                          T *B, int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s)
+{
+    using R = typename traits<T>::real;
+    hipError_t e = hipSuccess;
+    if (!is_one(alpha)) {
+        e = scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, false, s);
+        if (e != hipSuccess) return e;
+    }
+    T one = zero_of(T());
+    if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
+    for (int64_t r0 = 0; r0 < m; r0 += 64) {
+        const int64_t rows = m - r0 < 64 ? m - r0 : 64;
+        if (r0 > 0) {
+            e = gemm_strided<T>(rows, n, r0, R(-1), A + r0, lda, strideA, B, ldb, strideB, R(1),
+                                B + r0, ldb, strideB, batch, s);
+            if (e != hipSuccess) return e;
+        }
+        e = small_path<T>(rows, n, one, A + r0 + r0 * lda, lda, strideA, B + r0, ldb, strideB,
+                          batch, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <typename T>
 hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
                       T *B, int64_t ldb, int64_t strideB, int64_t batch,
@@ -212,6 +244,8 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     const int path = opts ? opts->path : HSMA_PATH_AUTO;
     const bool small = path == HSMA_PATH_SMALL || (path == HSMA_PATH_AUTO && m <= 64);
     if (small) return hip_status(small_path<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
+    if (path == HSMA_PATH_AUTO && batch > 1 && m <= kMediumMaxM)
+        return hip_status(medium_batched<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
 
     // Blocked path.
     int nb = (opts && opts->nb) ? opts->nb : choose_nb(dt, m);

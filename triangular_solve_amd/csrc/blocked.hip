@@ -582,6 +582,23 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
 }
 
 template <typename T>
+hipError_t gemm_strided(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
+                        const T *A, int64_t lda, int64_t strideA, const T *B, int64_t ldb,
+                        int64_t strideB, typename traits<T>::real beta, T *C, int64_t ldc,
+                        int64_t strideC, int64_t batch, hipStream_t s)
+{
+    const int64_t kMaxZ = 65535;  // grid z
+    for (int64_t b0 = 0; b0 < batch; b0 += kMaxZ) {
+        const int64_t nb = batch - b0 < kMaxZ ? batch - b0 : kMaxZ;
+        hipError_t e = gemm_batched<T>(M, N, K, alpha, A + b0 * strideA, lda, strideA, 0,
+                                       B + b0 * strideB, ldb, strideB, 0, beta, C + b0 * strideC,
+                                       ldc, strideC, 0, nb, nb, false, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename T>
 hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
                 int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
                 int64_t ldc, bool a_lower, hipStream_t s)
@@ -731,6 +748,10 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     template hipError_t gemm<T>(int64_t, int64_t, int64_t, typename traits<T>::real, const T *,    \
                                 int64_t, const T *, int64_t, typename traits<T>::real, T *,       \
                                 int64_t, bool, hipStream_t);                                      \
+    template hipError_t gemm_strided<T>(int64_t, int64_t, int64_t, typename traits<T>::real,       \
+                                        const T *, int64_t, int64_t, const T *, int64_t, int64_t, \
+                                        typename traits<T>::real, T *, int64_t, int64_t, int64_t, \
+                                        hipStream_t);                                             \
     template hipError_t blocked_solve<T>(int64_t, int64_t, int, int, const T *, int64_t, T *,     \
                                          int64_t, T *, hipStream_t);
 HSMA_INST(float)

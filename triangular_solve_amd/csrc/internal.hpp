@@ -62,6 +62,14 @@ hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
                 int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
                 int64_t ldc, bool a_lower, hipStream_t s);
 
+// Strided-batched C_z = beta*C_z + alpha*A_z*B_z, z < batch (A_z = A + z*strideA,
+// alike for B and C; strideA may be 0).
+template <typename T>
+hipError_t gemm_strided(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
+                        const T *A, int64_t lda, int64_t strideA, const T *B, int64_t ldb,
+                        int64_t strideB, typename traits<T>::real beta, T *C, int64_t ldc,
+                        int64_t strideC, int64_t batch, hipStream_t s);
+
 // Whole blocked solve of one problem (B already scaled by alpha), with a
 // caller-provided workspace of blocked_workspace_elems(m, n, nb) elements.
 int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb);
