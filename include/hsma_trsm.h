@@ -169,13 +169,19 @@ hsma_status hsma_trsm_ex_z(int64_t m, int64_t n, hsma_double_complex alpha,
  *
  * hsma_diag_inv_{s,d,c,z}: inverts every diagonal block of the lower
  * triangle of A (HSMA-TRSM paper, blocked section: the diagonal blocks D_t
- * are independent and are inverted in parallel, each by substitution against
- * identity tiles E_j of width ib). Block t covers rows/columns
- * [t*nb, min(m, (t+1)*nb)). invA receives ceil(m/nb) blocks of nb x nb,
- * block t at invA + t*nb*nb, column-major with leading dimension nb; entries
- * above the diagonal, and rows/columns beyond m in the last block, are
- * written as exact zeros (the padded part of the last block holds the
- * identity on its diagonal). nb, ib as in hsma_trsm_opts (0 = defaults).
+ * are independent and are inverted in parallel, by substitution against
+ * identity tiles). Block t covers rows/columns [t*nb, min(m, (t+1)*nb)).
+ * invA receives ceil(m/nb) blocks of nb x nb, block t at invA + t*nb*nb,
+ * column-major with leading dimension nb; entries above the diagonal, and
+ * rows/columns beyond m in the last block, are written as exact zeros (the
+ * padded part of the last block holds the identity on its diagonal).
+ * nb, ib as in hsma_trsm_opts (0 = defaults). When m is a multiple of nb and
+ * nb a multiple of 64 with nb >= 128, 64 x 64 sub-blocks are inverted by
+ * substitution against identity columns and merged by the block-inverse
+ * formula with matrix-core products (ib unused; a temporary of nb*nb/4
+ * elements per block comes from the library's workspace pool); otherwise
+ * column-level substitution against identity tiles of width ib (nb <= 1024).
+ * Either way the result is the block inverses up to rounding.
  */
 hsma_status hsma_diag_inv_s(int64_t m, int32_t nb, int32_t ib, const float *A, int64_t lda,
                             float *invA, void *stream);
@@ -187,7 +193,7 @@ hsma_status hsma_diag_inv_z(int64_t m, int32_t nb, int32_t ib, const hsma_double
                             int64_t lda, hsma_double_complex *invA, void *stream);
 
 /*
- * hsma_gemm_{s,d,c,z}: C = beta*C + alpha*op(A)*B with A M x K, B K x N,
+ * hsma_gemm_{s,d,c,z}: C = beta*C + alpha*A*B with A M x K, B K x N,
  * C M x N, all column-major, on the matrix cores (the update of the trailing
  * rows and the multiply by an inverted diagonal block in the blocked path).
  * alpha and beta are real, beta must be 0 or 1 (beta == 0: C is not read).
