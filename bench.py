@@ -240,6 +240,78 @@ def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0):
     return out
 
 
+def medium_workload(hs, torch, m=128, n=64, batch=1024, reps=5):
+    """Strided batches in the 64 < m <= 256 band (block rows of 64 over the
+    whole batch): ms per batched call and GFLOPS per dtype, plus 64-problem
+    parity against the oracle."""
+    import oracle
+    import synth
+    out = {}
+    stream = torch.cuda.current_stream()
+    for dt in DTYPES:
+        A = synth.tri(dt, m, batch, seed=SEED_CFG1)
+        B = synth.rhs(dt, m, n, batch, seed=SEED_CFG1 + 1)
+        dA, dB0 = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dB = dB0.clone()
+        f = hs.entry("strided_batched", dt)
+        times = []
+        for r in range(reps + 1):
+            dB.copy_(dB0)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hs.check(f(m, n, 1.0, dA, m, m * m, dB, m, m * n, batch, stream), "strided_batched_" + dt)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = float(np.mean(times[1:]))
+        Xg = dB[:64].cpu().numpy()[:, :, :m].transpose(0, 2, 1)
+        Xo = oracle.trsm(A[:64, :, :m].transpose(0, 2, 1), B[:64, :, :m].transpose(0, 2, 1))
+        err = float(np.max([np.linalg.norm(Xg[i] - Xo[i]) / np.linalg.norm(Xo[i]) for i in range(64)]))
+        out[dt] = {"ms": ms, "gflops": lapack_flops(dt, m, n) * batch / (ms * 1e6), "rel_err_64": err}
+        del dA, dB, dB0
+    return out
+
+
+def gemm_workload(hs, torch, shapes=((7168, 8192, 1024), (6144, 8192, 2048)), reps=5):
+    """The library GEMM at trailing-update shapes of the blocked solve
+    (C -= A B, beta = 1), per dtype, against torch's own matmul on the same
+    shapes for context (not part of any path)."""
+    out = {}
+    stream = torch.cuda.current_stream()
+    tdt = {"f32": torch.float32, "f64": torch.float64, "c64": torch.complex64, "c128": torch.complex128}
+    torch.backends.cuda.matmul.allow_tf32 = False
+    for dt in DTYPES:
+        for (M, N, K) in shapes:
+            g = torch.Generator(device="cuda").manual_seed(M + K)
+            A = torch.rand(K, M, device="cuda", generator=g, dtype=tdt[dt])   # column-major M x K
+            Bm = torch.rand(N, K, device="cuda", generator=g, dtype=tdt[dt])  # column-major K x N
+            C = torch.rand(N, M, device="cuda", generator=g, dtype=tdt[dt])
+            f = hs.entry("gemm", dt)
+
+            def timed(fn):
+                fn()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / reps
+
+            ms = timed(lambda: hs.check(f(M, N, K, -1.0, A, M, Bm, K, 1.0, C, M, 0, stream), "gemm_" + dt))
+            Ct, At, Bt = C.t(), A.t(), Bm.t()
+            ms_t = timed(lambda: Ct.addmm_(At, Bt, alpha=-1))
+            flops = (8 if dt.startswith("c") else 2) * M * N * K
+            peak = MFMA_PEAK_TFLOPS[dt]
+            out["%s %dx%dx%d" % (dt, M, N, K)] = {
+                "ms": ms, "tflops": flops / ms / 1e9, "mfma_peak_frac": flops / ms / 1e9 / peak,
+                "torch_ms": ms_t, "torch_mfma_peak_frac": flops / ms_t / 1e9 / peak}
+            del A, Bm, C
+    return out
+
+
 def counter_workload(hs, torch):
     """Three batched solves per dtype (4096 problems, m = n = 64), then a 1 GiB
     device-to-device copy whose byte counts calibrate the HBM counters."""
@@ -299,9 +371,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="batched", choices=["batched", "blocked", "counters"],
+    ap.add_argument("--workload", default="batched",
+                    choices=["batched", "blocked", "counters", "medium", "gemm"],
                     help="counters: only three batched solves per dtype and a 1 GiB copy, for "
-                         "rocprofv3 --pmc runs")
+                         "rocprofv3 --pmc runs; medium: strided batches of 1024 systems with "
+                         "m = 128, n = 64; gemm: the library GEMM at trailing-update shapes")
     ap.add_argument("--m", type=int, default=8192, help="blocked workload size (m = n)")
     ap.add_argument("--dtypes", default="f32,f64,c64,c128")
     ap.add_argument("--nb", type=int, default=0, help="blocked N_B override (0: table)")
@@ -322,6 +396,10 @@ def main():
 
     if args.workload == "counters":
         counter_workload(hs, torch)
+        return
+    if args.workload in ("medium", "gemm"):
+        res = medium_workload(hs, torch) if args.workload == "medium" else gemm_workload(hs, torch)
+        print(json.dumps({"workload": args.workload, "results": res}), flush=True)
         return
     if args.workload == "blocked":
         dts = args.dtypes.split(",")
