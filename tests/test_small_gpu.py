@@ -173,8 +173,10 @@ def test_solve_tri_medium_sizes(hs):
     """64 < n <= 256: block rows of 64 (the PR's [128,128,4,1] / [8,128,4,1]
     case included), ragged last blocks, k above and below the 8-column
     update groups."""
-    for (n, k, e2, e3) in [(128, 8, 4, 1), (100, 5, 2, 3), (65, 1, 1, 1), (256, 6, 1, 2),
-                           (200, 130, 1, 1), (192, 64, 2, 1)]:
+    # n <= 128: one launch, 2 / 4 / 8 columns per workgroup for k <= 8 / <= 32 / more;
+    # n > 128: block rows of 64
+    for (n, k, e2, e3) in [(128, 8, 4, 1), (100, 5, 2, 3), (65, 1, 1, 1), (96, 20, 2, 1),
+                           (128, 70, 1, 2), (256, 6, 1, 2), (200, 130, 1, 1), (192, 64, 2, 1)]:
         say("solve_tri medium", n, k, e2, e3)
         X, Xo, A, B = ggml_case(hs, n, k, e2, e3, seed=n + 3 * k)
         assert rel_err(X, Xo) <= TOL_SMALL["f32"]
@@ -185,7 +187,7 @@ def test_solve_tri_medium_sizes(hs):
 # n = 48: rows staged through LDS; n = 64 with 16-byte aligned row strides:
 # rows of A kept in registers; n = 64 with odd strides: back to LDS staging
 @pytest.mark.parametrize("n,sA1,pa2,pa3", [(48, 50, 5, 7), (64, 68, 4, 8), (64, 65, 5, 7),
-                                           (150, 152, 4, 8), (130, 131, 5, 7)])
+                                           (150, 152, 4, 8), (130, 131, 5, 7), (100, 103, 5, 7)])
 def test_solve_tri_strided_views(hs, n, sA1, pa2, pa3):
     """Non-contiguous batches: A, B, X inside larger buffers with padded strides."""
     import torch
