@@ -354,12 +354,13 @@ struct PanelPlan {
     static constexpr Table T = build();
 };
 
-// The diagonal travels with the coefficient stream for f32, whose
-// reciprocal is one v_rcp_f32 on the scalar value (within an ulp). For the
-// other types a full-precision reciprocal per column would cost several
-// instructions, so every lane computes 1/a_ll of its row once at the start.
+// The diagonal travels with the coefficient stream for the real types: f32
+// takes one v_rcp_f32 of the scalar value (within an ulp), f64 v_rcp_f64
+// refined by two Newton steps. For the complex types a reciprocal per column
+// would cost more instructions, so every lane computes 1/a_ll of its row
+// once at the start.
 template <typename T>
-constexpr bool kDiagInStream = std::is_same<T, float>::value;
+constexpr bool kDiagInStream = std::is_same<T, float>::value || std::is_same<T, double>::value;
 
 // Coefficients per batch: 64 dwords of SGPRs.
 template <typename T>
@@ -598,6 +599,15 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
                 if constexpr (std::is_same<T, float>::value) {
                     float r = __builtin_amdgcn_rcpf(cb[off]);
                     asm volatile("" : "+v"(r) : "v"(st.w[j]));
+                    st.x = st.w[j] * r;
+                } else if constexpr (std::is_same<T, double>::value) {
+                    const double dv = cb[off];
+                    double r = __builtin_amdgcn_rcp(dv);
+                    asm volatile("" : "+v"(r) : "v"(st.w[j]));
+                    double e = __builtin_fma(-dv, r, 1.0);
+                    r = __builtin_fma(r, e, r);
+                    e = __builtin_fma(-dv, r, 1.0);
+                    r = __builtin_fma(r, e, r);
                     st.x = st.w[j] * r;
                 }
                 st.w[j] = st.x;
