@@ -75,3 +75,30 @@ def test_medium_batched_exact_integer(hs):
     assert hs.hsma_trsm_strided_batched_d(m, n, 1.0, dA, m, 0, dB, m, m * n, batch) == hs.SUCCESS
     torch.cuda.synchronize()
     assert np.array_equal(dB.cpu().numpy().transpose(0, 2, 1), np.cumsum(Bm, axis=1))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("m,n", [(64, 64), (40, 9), (128, 64), (200, 33)])
+def test_batch_member_equals_solo_solve(hs, dtype, m, n):
+    """A problem's result inside a strided batch is bitwise the one it gets when
+    solved as a batch of one: nothing in a problem's arithmetic depends on its
+    neighbours (small regime and block rows alike)."""
+    import torch
+    batch = 6
+    A, B = colmajor_inputs(dtype, m, n, batch, seed=21 + m + n)
+    dA, dB = to_dev(A), to_dev(B)
+    f = hs.entry("strided_batched", dtype)
+    assert f(m, n, 1.0, dA, m, m * m, dB, m, m * n, batch) == hs.SUCCESS
+    for p in (0, 3, 5):
+        dA1, dB1 = to_dev(A[p:p + 1]), to_dev(B[p:p + 1])
+        assert f(m, n, 1.0, dA1, m, m * m, dB1, m, m * n, 1) == hs.SUCCESS
+        torch.cuda.synchronize()
+        solo = dB1.cpu().numpy()[0]
+        if m > 64:
+            # a batch of one takes the blocked path, whose rounding differs: compare
+            # against a batch of two holding the same problem twice instead
+            dA2, dB2 = to_dev(np.concatenate([A[p:p + 1]] * 2)), to_dev(np.concatenate([B[p:p + 1]] * 2))
+            assert f(m, n, 1.0, dA2, m, m * m, dB2, m, m * n, 2) == hs.SUCCESS
+            torch.cuda.synchronize()
+            solo = dB2.cpu().numpy()[1]
+        assert np.array_equal(dB.cpu().numpy()[p], solo)
