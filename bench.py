@@ -10,8 +10,11 @@ value = LAPACK-count GFLOPS of the whole step (m^2 n per real problem,
 every step solves distinct copies of A and B (a ring larger than the 256 MB
 MALL), so no step reads another step's data from cache.
 
-The same line carries the blocked regime at m = n = 8192 (one solve per
-dtype, LAPACK GFLOPS and the MFMA-peak fraction), the SOLVE_TRI shape
+The same line carries the blocked regime at m = n = 8192 (f32, f64, c64, c128)
+and m = n = 16384 (f32, f64, c128): one solve per dtype, LAPACK GFLOPS, the
+MFMA-peak fraction, the time split between diagonal inversion, GEMMs and the
+rest measured inside one solve, 64-column parity and the oracle's time on
+those columns. Then the SOLVE_TRI shape
 (8 systems of 64 x 64 with 6 right-hand sides, ggml layout, us per call), the
 roofline of the dominant kernel, and the CPU oracle timed on the same step.
 
@@ -186,8 +189,42 @@ def bench_solve_tri(hs, torch, runs=2000, n=64, k=6, e2=4, e3=2):
             "launches_timed": runs}
 
 
-def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0):
-    """One blocked solve per dtype at m = n, restored B between runs (untimed)."""
+def phase_split(hs, torch, f, m, dt, dA, dB, nbu, stream):
+    """One blocked solve with the library's phase events: ms per phase, in
+    the solve's own launch order (events recorded by the library between
+    its launches on the stream)."""
+    import ctypes
+    nt = (m + nbu - 1) // nbu
+    cap = 3 * nt + 2
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(cap)]
+    for e in evs:            # creates the underlying HIP events
+        e.record(stream)
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * cap)(*[e.cuda_event for e in evs])
+    phases = (ctypes.c_int32 * cap)()
+    used = ctypes.c_int32(0)
+    opts = hs.TrsmOpts(nbu, 0, hs.PATH_BLOCKED, cap, handles, phases, ctypes.pointer(used))
+    hs.check(f(m, m, 1.0, dA, m, dB, m, opts, stream), "trsm_ex_" + dt + " (timed phases)")
+    torch.cuda.synchronize()
+    out = {name: 0.0 for name in hs.PHASE_NAMES.values()}
+    for k in range(used.value - 1):
+        out[hs.PHASE_NAMES[phases[k]]] += evs[k].elapsed_time(evs[k + 1])
+    total = evs[0].elapsed_time(evs[used.value - 1])
+    gemm = out["inv_gemm"] + out["trailing_gemm"]
+    other = total - gemm - out["diag_inv"]
+    return {"ms_with_events": total, "phase_ms": out, "events": used.value,
+            "share": {"diag_inv": out["diag_inv"] / total, "gemm": gemm / total,
+                      "other": other / total},
+            "share_note": "gemm = inverse-block multiplies + trailing updates; other = W->B copies, "
+                          "scaling and launch gaps"}
+
+
+def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0, cpu=True):
+    """One blocked solve per dtype at m = n, B restored between runs (untimed);
+    the phase split from a separate run with the library's phase events; 64
+    seeded columns against the oracle, whose time on those columns is the
+    configuration's CPU baseline."""
+    import oracle
     import synth
     out = {}
     stream = torch.cuda.current_stream()
@@ -198,7 +235,8 @@ def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0):
         dA, dB0 = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
         dB = dB0.clone()
         f = hs.entry("ex", dt)
-        opts = {"nb": nb, "path": hs.PATH_BLOCKED}
+        nbu = nb or hs.hsma_trsm_block_size(hs.DTYPE_CODE[dt], m)
+        opts = {"nb": nbu, "path": hs.PATH_BLOCKED}
         times = []
         for r in range(runs + 1):     # first run is a warm-up
             dB.copy_(dB0)
@@ -213,29 +251,32 @@ def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0):
             times.append(a.elapsed_time(b))
         ms = float(np.mean(times[1:]))
         # sampled parity: 64 seeded columns against the oracle
-        import oracle
         cols = synth.pick_columns(m, 64, seed=SEED_CFG3)
         Xg = dB[0, torch.from_numpy(cols).cuda()].cpu().numpy().T
-        Xo = oracle.trsm(A[0].T, B[0, cols].T)
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        Xo = oracle.trsm(A[0].T, B[0, cols].T, threads=threads)
+        osec = time.perf_counter() - t0
         err = float(np.linalg.norm(Xg.astype(Xo.dtype) - Xo) / np.linalg.norm(Xo))
-        # diagonal-inversion share: the inversion alone, same N_B
-        nbu = nb or hs.hsma_trsm_block_size(hs.DTYPE_CODE[dt], m)
-        nt = (m + nbu - 1) // nbu
-        inv = torch.empty(nt * nbu * nbu, dtype=dB.dtype, device="cuda")
-        dts = []
-        for r in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            hs.entry("diag_inv", dt)(m, nbu, nbu // 8, dA, m, inv, stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            dts.append(a.elapsed_time(b))
-        inv_ms = float(np.mean(dts[1:]))
+        dB.copy_(dB0)
+        split = phase_split(hs, torch, f, m, dt, dA, dB, nbu, stream)
         flops = lapack_flops(dt, m, m)
         out[dt] = {"ms": ms, "gflops": flops / ms / 1e6, "nb": nbu,
                    "mfma_peak_frac": flops / ms / 1e9 / MFMA_PEAK_TFLOPS[dt],
-                   "diag_inv_ms": inv_ms, "diag_inv_share": inv_ms / ms, "rel_err_64cols": err}
-        del dA, dB0, dB, inv, A, B
+                   "phases": split, "rel_err_64cols": err,
+                   "cpu_baseline": {
+                       "value": lapack_flops(dt, m, 64) / osec / 1e9, "unit": "GFLOPS",
+                       "cores": threads, "kind": "oracle",
+                       "sample": "64 seeded right-hand-side columns of the m=n=%d %s solve, plain C "
+                                 "double-precision forward substitution, %d threads on %s"
+                                 % (m, dt, threads, cpu_model()),
+                       "seconds_64cols": osec,
+                       "extrapolated_full_n_seconds": osec * m / 64,
+                       "extrapolation_note": "seconds_64cols x n/64, not measured"}}
+        log("  %.3f ms, %.1f%% of MFMA peak, split %s" % (
+            ms, 100 * out[dt]["mfma_peak_frac"],
+            {k: round(v, 3) for k, v in split["share"].items()}))
+        del dA, dB0, dB, A, B
         torch.cuda.empty_cache()
     return out
 
@@ -429,9 +470,10 @@ def main():
     st = bench_solve_tri(hs, torch)
     log("solve_tri 128 shape")
     st128 = bench_solve_tri(hs, torch, runs=1000, n=128, k=8, e2=4, e3=1)
-    blocked = None
+    blocked = blocked16 = None
     if not args.no_blocked:
         blocked = bench_blocked(hs, torch, 8192, DTYPES, runs=3)
+        blocked16 = bench_blocked(hs, torch, 16384, ["f32", "f64", "c128"], runs=2)
     cpu = None if args.no_cpu else cpu_baseline(bt["host"])
     line = {
         "metric": METRIC, "value": bt["gflops"], "unit": "GFLOPS", "n_gpus": 1, "steps": args.steps,
@@ -447,6 +489,7 @@ def main():
         "per_dtype": per,
         "solve_tri": st, "solve_tri_128": st128,
         "blocked_8192": blocked,
+        "blocked_16384": blocked16,
     }
     print(json.dumps(line), flush=True)
 

@@ -31,7 +31,16 @@
  *     workspace used so far) instead of being returned to the driver.
  *   - No singularity check: a zero or NaN diagonal entry produces inf/NaN
  *     under IEEE rules (the SOLVE_TRI review in llama.cpp PR #17457 dropped
- *     its zero-pivot guard for the same reason).
+ *     its zero-pivot guard for the same reason). Pivots are applied as
+ *     reciprocals, x_j = w_j * (1/a_jj): a zero pivot gives +-inf (NaN where
+ *     w_j is 0 or the pivot is complex) in its row and non-finite values in
+ *     every row below it, in every path. A pivot whose reciprocal overflows
+ *     (|a_jj| < 2^-1024 in double; subnormal float pivots) acts like a zero
+ *     pivot. Complex reciprocals are scaled (Smith's method), so they hold
+ *     over the whole exponent range.
+ *   - The environment variable HSMA_TEST_FAIL_ALLOC=1 makes every workspace
+ *     allocation fail: such calls return ALLOC_FAILED before any GPU work
+ *     (for tests of that error path).
  *   - m == 0, n == 0 or batch_count == 0: success, no memory touched.
  *     alpha == 0: B is set to zero and A is not read.
  *   - No C++ exception crosses this interface.
@@ -86,6 +95,10 @@ hsma_status hsma_trsm_z(int64_t m, int64_t n, hsma_double_complex alpha,
 /*
  * hsma_trsm_strided_batched_{s,d,c,z}: batch_count independent systems;
  * problem b uses A + b*strideA and B + b*strideB (strides in elements).
+ * The batched use case is llama.cpp's SOLVE_TRI (PR #17457, "SOLVE_TRI CUDA
+ * kernel for small matrices": one small system per batch index, solved by one
+ * thread block each); the HSMA-TRSM paper's small-scale section gives the
+ * per-problem method (the triangle on chip, direct solve).
  * strideA == 0 shares one A across the batch. B blocks must not overlap:
  * strideB >= ldb*n when batch_count > 1 (else INVALID_SIZE).
  * m <= 64 runs as one launch over the whole batch (the pages' small regime);
@@ -93,6 +106,7 @@ hsma_status hsma_trsm_z(int64_t m, int64_t n, hsma_double_complex alpha,
  * one batched GEMM update with the finished rows and one batched small-regime
  * solve of the diagonal blocks); larger m runs the blocked solver once per
  * problem.
+ * Errors: as hsma_trsm_*; ALLOC_FAILED only for m > 256.
  */
 hsma_status hsma_trsm_strided_batched_s(int64_t m, int64_t n, float alpha, const float *A,
                                         int64_t lda, int64_t strideA, float *B, int64_t ldb,
@@ -134,24 +148,57 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
                                int64_t sX3, void *stream);
 
 /*
- * Options for the *_ex entry points (a NULL opts means all defaults).
+ * Options for the *_ex entry points (a NULL opts means all defaults). They
+ * exist for the offline block-size sweep of the HSMA-TRSM paper's adaptive
+ * blocking section (every candidate block size is run and timed on the
+ * target GPU) and for tests of each route.
  *   nb    outer block size N_B of the blocked path (0: from the built-in
  *         table); must be a multiple of 16 in [16, 2048]; above 1024 (above
  *         512 for double complex) m must also be a multiple of nb, since
  *         such blocks are inverted only by the blocked-inverse formula
- *   ib    inner block size I_B of the diagonal inversion (0: nb/8); must
- *         divide nb, and nb/ib <= 64
+ *   ib    inner block I_B of the diagonal inversion (0: nb/8; must divide nb,
+ *         nb/ib <= 64). The paper's I_B is the width of the identity tile a
+ *         work unit substitutes against (blocked section). Here it only
+ *         applies to the column-substitution route (m not a multiple of nb,
+ *         or nb < 128): a work unit takes the largest power of two G <= 16
+ *         (<= 8 for double and float complex, <= 4 for double complex; the
+ *         register budget) that divides both ib and nb. The blocked-inverse
+ *         route always starts from 64 x 64 sub-blocks (the small-regime
+ *         solver's size) and ignores ib.
  *   path  HSMA_PATH_AUTO, HSMA_PATH_SMALL (requires m <= 64) or
  *         HSMA_PATH_BLOCKED (any m >= 1)
+ *   Timing of the blocked path's phases (the paper's Table 3 splits the
+ *   run time into diagonal inversion and GEMM update): when n_events > 0,
+ *   events[0 .. n_events) are hipEvent_t handles created by the caller, and
+ *   the library records events[k] on the stream at the start of each phase
+ *   and once more at the end, writing the phase code (HSMA_PHASE_*) of the
+ *   interval that starts at events[k] to event_phase[k] (HSMA_PHASE_END for
+ *   the last event) and the number of events recorded to *events_used. The
+ *   interval between events[k] and events[k+1] is then the time of phase
+ *   event_phase[k]. A blocked solve records 3*ceil(m/nb) + 1 events, one
+ *   more when alpha != 1; if n_events is smaller the call returns
+ *   INVALID_VALUE before any work, with the number needed in *events_used.
+ *   Events are recorded only by the blocked path (*events_used = 0 on the
+ *   others). event_phase and events_used must be valid when n_events > 0.
  * Bad values return INVALID_VALUE.
  */
 #define HSMA_PATH_AUTO 0
 #define HSMA_PATH_SMALL 1
 #define HSMA_PATH_BLOCKED 2
+#define HSMA_PHASE_END (-1)
+#define HSMA_PHASE_SCALE 0      /* B := alpha * B */
+#define HSMA_PHASE_DIAG_INV 1   /* inversion of all diagonal blocks */
+#define HSMA_PHASE_INV_GEMM 2   /* W = D_t^{-1} B_t */
+#define HSMA_PHASE_COPY 3       /* W -> B_t */
+#define HSMA_PHASE_TRAILING 4   /* B[below] -= A[below, t] X_t */
 typedef struct {
     int32_t nb;
     int32_t ib;
     int32_t path;
+    int32_t n_events;
+    void **events;
+    int32_t *event_phase;
+    int32_t *events_used;
 } hsma_trsm_opts;
 
 hsma_status hsma_trsm_ex_s(int64_t m, int64_t n, float alpha, const float *A, int64_t lda,
@@ -182,7 +229,9 @@ hsma_status hsma_trsm_ex_z(int64_t m, int64_t n, hsma_double_complex alpha,
  * substitution against identity columns and merged by the block-inverse
  * formula with matrix-core products (ib unused; a temporary of nb*nb/4
  * elements per block comes from the library's workspace pool); otherwise
- * column-level substitution against identity tiles of width ib (nb <= 1024).
+ * column-level substitution, one work unit per (diagonal block, group of G
+ * identity columns) with G chosen from ib as described for hsma_trsm_opts
+ * (nb <= 1024).
  * Either way the result is the block inverses up to rounding.
  */
 hsma_status hsma_diag_inv_s(int64_t m, int32_t nb, int32_t ib, const float *A, int64_t lda,

@@ -24,10 +24,14 @@ def to_dev(arr):
 
 
 def rel_err(Xg, Xo):
-    """Max over problems of ||Xg - Xo||_F / ||Xo||_F (arrays [batch, m, n])."""
+    """Max over problems of ||Xg - Xo||_F / ||Xo||_F (arrays [batch, m, n]),
+    both scaled by the problem's largest |Xo| first so that the squares
+    cannot overflow."""
     Xg = Xg.astype(Xo.dtype)
-    num = np.sqrt(np.sum(np.abs(Xg - Xo) ** 2, axis=(-2, -1)))
-    den = np.sqrt(np.sum(np.abs(Xo) ** 2, axis=(-2, -1)))
+    sc = np.max(np.abs(Xo), axis=(-2, -1), keepdims=True)
+    sc = np.where(sc == 0, 1.0, sc)
+    num = np.sqrt(np.sum(np.abs((Xg - Xo) / sc) ** 2, axis=(-2, -1)))
+    den = np.sqrt(np.sum(np.abs(Xo / sc) ** 2, axis=(-2, -1)))
     den = np.where(den == 0, 1.0, den)
     return float(np.max(num / den))
 

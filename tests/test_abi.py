@@ -118,3 +118,36 @@ def test_block_size_table(hs):
             assert nb <= ((m + 15) // 16) * 16
             assert nb <= (512 if code == 3 else 1024) or m % nb == 0
     assert hs.hsma_trsm_block_size(7, 100) == -1
+
+
+@pytest.mark.parametrize("t", ["f32", "f64", "c64", "c128"])
+def test_alloc_failure_injection(hs, t, monkeypatch):
+    """HSMA_TEST_FAIL_ALLOC=1 makes the workspace allocation fail: the blocked
+    path and the diagonal inversion return ALLOC_FAILED before any GPU work
+    (the pointers below are never dereferenced)."""
+    monkeypatch.setenv("HSMA_TEST_FAIL_ALLOC", "1")
+    assert hs.entry("trsm", t)(300, 8, 1, BAD, 300, BAD, 300, 0) == hs.ALLOC_FAILED
+    assert hs.entry("ex", t)(300, 8, 1, BAD, 300, BAD, 300, {"nb": 128, "path": hs.PATH_BLOCKED},
+                             0) == hs.ALLOC_FAILED
+    assert hs.entry("strided_batched", t)(300, 8, 1, BAD, 300, 0, BAD, 300, 2400, 3, 0) == hs.ALLOC_FAILED
+    assert hs.entry("diag_inv", t)(1024, 256, 0, BAD, 1024, BAD, 0) == hs.ALLOC_FAILED
+    assert hs.hsma_status_string(hs.ALLOC_FAILED) == "workspace allocation failed"
+
+
+def test_phase_event_checks(hs):
+    """Phase-event options are validated before any GPU work: too few events
+    returns INVALID_VALUE with the count needed."""
+    import ctypes
+    used = ctypes.c_int32(-5)
+    phases = (ctypes.c_int32 * 4)()
+    evs = (ctypes.c_void_p * 4)()
+    o = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 4, evs, phases, ctypes.pointer(used))
+    # m = 1000, nb = 128: 8 diagonal blocks -> 3*8 + 1 events (+1 with alpha != 1)
+    assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, o, 0) == hs.INVALID_VALUE
+    assert used.value == 25
+    assert hs.entry("ex", "f64")(1000, 4, 2, BAD, 1000, BAD, 1000, o, 0) == hs.INVALID_VALUE
+    assert used.value == 26
+    bad = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 4, evs, None, ctypes.pointer(used))
+    assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, bad, 0) == hs.INVALID_POINTER
+    neg = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, -1, None, None, None)
+    assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, neg, 0) == hs.INVALID_VALUE

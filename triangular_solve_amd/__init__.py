@@ -5,26 +5,18 @@ returns the C status code (0 = success). Array arguments are device pointers:
 pass torch CUDA tensors (their data_ptr() is used) or plain integers.
 `stream` is a torch.cuda.Stream, a raw hipStream_t integer, or None for
 torch's current stream. All compute happens in the HIP library; there is no
-fallback: importing this module fails if the library has not been built.
+fallback: the first call raises if the library has not been built.
+
+The library is loaded on first use, not at import, so that the build module
+(triangular_solve_amd.build) can be imported and run from a checkout that has
+no built library yet. A process that has loaded the library keeps that
+mapping: rebuild before the first call, not after it.
 """
 import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsma_trsm.so")
-
-if not os.path.exists(LIB_PATH):
-    raise ImportError("libhsma_trsm.so is not built; run `python -m triangular_solve_amd.build` "
-                      "(or __graft_entry__.build()) first")
-
-# Load torch first when it is installed: its bundled HIP runtime then serves
-# this library too (same soname), so torch's streams and allocations are ours.
-try:
-    import torch as _torch  # noqa: F401
-except ImportError:  # pragma: no cover
-    _torch = None
-
-_lib = ctypes.CDLL(LIB_PATH)
 
 SUCCESS = 0
 INVALID_SIZE = 1
@@ -37,6 +29,11 @@ INVALID_VALUE = 6
 DTYPE_F32, DTYPE_F64, DTYPE_C64, DTYPE_C128 = 0, 1, 2, 3
 PATH_AUTO, PATH_SMALL, PATH_BLOCKED = 0, 1, 2
 
+# Phase codes of the blocked path's timing events (hsma_trsm_opts.events).
+PHASE_END, PHASE_SCALE, PHASE_DIAG_INV, PHASE_INV_GEMM, PHASE_COPY, PHASE_TRAILING = -1, 0, 1, 2, 3, 4
+PHASE_NAMES = {PHASE_SCALE: "scale", PHASE_DIAG_INV: "diag_inv", PHASE_INV_GEMM: "inv_gemm",
+               PHASE_COPY: "copy", PHASE_TRAILING: "trailing_gemm"}
+
 
 class FloatComplex(ctypes.Structure):
     _fields_ = [("re", ctypes.c_float), ("im", ctypes.c_float)]
@@ -47,7 +44,10 @@ class DoubleComplex(ctypes.Structure):
 
 
 class TrsmOpts(ctypes.Structure):
-    _fields_ = [("nb", ctypes.c_int32), ("ib", ctypes.c_int32), ("path", ctypes.c_int32)]
+    _fields_ = [("nb", ctypes.c_int32), ("ib", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("n_events", ctypes.c_int32), ("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("event_phase", ctypes.POINTER(ctypes.c_int32)),
+                ("events_used", ctypes.POINTER(ctypes.c_int32))]
 
 
 class HsmaError(RuntimeError):
@@ -60,30 +60,60 @@ _i64, _i32, _p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 _SCAL = {"s": ctypes.c_float, "d": ctypes.c_double, "c": FloatComplex, "z": DoubleComplex}
 _REAL = {"s": ctypes.c_float, "d": ctypes.c_double, "c": ctypes.c_float, "z": ctypes.c_double}
 
-
-def _proto(name, args, res=ctypes.c_int):
-    f = getattr(_lib, name)
-    f.argtypes = args
-    f.restype = res
-    return f
-
-
-_F = {}
+# Prototype of every entry point: name -> (argument types, result type).
+_PROTO = {}
 for _t in "sdcz":
     S, Rl = _SCAL[_t], _REAL[_t]
-    _F["hsma_trsm_" + _t] = _proto("hsma_trsm_" + _t, [_i64, _i64, S, _p, _i64, _p, _i64, _p])
-    _F["hsma_trsm_strided_batched_" + _t] = _proto(
-        "hsma_trsm_strided_batched_" + _t, [_i64, _i64, S, _p, _i64, _i64, _p, _i64, _i64, _i64, _p])
-    _F["hsma_trsm_ex_" + _t] = _proto(
-        "hsma_trsm_ex_" + _t, [_i64, _i64, S, _p, _i64, _p, _i64, ctypes.POINTER(TrsmOpts), _p])
-    _F["hsma_diag_inv_" + _t] = _proto("hsma_diag_inv_" + _t, [_i64, _i32, _i32, _p, _i64, _p, _p])
-    _F["hsma_gemm_" + _t] = _proto(
-        "hsma_gemm_" + _t, [_i64, _i64, _i64, Rl, _p, _i64, _p, _i64, Rl, _p, _i64, _i32, _p])
-_F["hsma_solve_tri_f32"] = _proto("hsma_solve_tri_f32", [_i64, _i64, _p, _p, _p] + [_i64] * 11 + [_p])
-_F["hsma_trsm_block_size"] = _proto("hsma_trsm_block_size", [_i32, _i64], ctypes.c_int32)
-_F["hsma_status_string"] = _proto("hsma_status_string", [ctypes.c_int], ctypes.c_char_p)
+    _PROTO["hsma_trsm_" + _t] = ([_i64, _i64, S, _p, _i64, _p, _i64, _p], ctypes.c_int)
+    _PROTO["hsma_trsm_strided_batched_" + _t] = (
+        [_i64, _i64, S, _p, _i64, _i64, _p, _i64, _i64, _i64, _p], ctypes.c_int)
+    _PROTO["hsma_trsm_ex_" + _t] = (
+        [_i64, _i64, S, _p, _i64, _p, _i64, ctypes.POINTER(TrsmOpts), _p], ctypes.c_int)
+    _PROTO["hsma_diag_inv_" + _t] = ([_i64, _i32, _i32, _p, _i64, _p, _p], ctypes.c_int)
+    _PROTO["hsma_gemm_" + _t] = (
+        [_i64, _i64, _i64, Rl, _p, _i64, _p, _i64, Rl, _p, _i64, _i32, _p], ctypes.c_int)
+_PROTO["hsma_solve_tri_f32"] = ([_i64, _i64, _p, _p, _p] + [_i64] * 11 + [_p], ctypes.c_int)
+_PROTO["hsma_trsm_block_size"] = ([_i32, _i64], ctypes.c_int32)
+_PROTO["hsma_status_string"] = ([ctypes.c_int], ctypes.c_char_p)
 
-EXPORTS = sorted(_F)
+EXPORTS = sorted(_PROTO)
+
+_lib = None
+_F = {}
+
+
+def load():
+    """The loaded library (loaded on the first call). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhsma_trsm.so is not built; run `python -m triangular_solve_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        # Load torch first when it is installed: its bundled HIP runtime then
+        # serves this library too (same soname), so torch's streams and
+        # allocations are valid here.
+        try:
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover
+            pass
+        _lib = ctypes.CDLL(LIB_PATH)
+    return _lib
+
+
+def loaded():
+    """Whether this process has loaded the library."""
+    return _lib is not None
+
+
+def _fn(name):
+    f = _F.get(name)
+    if f is None:
+        args, res = _PROTO[name]
+        f = getattr(load(), name)
+        f.argtypes = args
+        f.restype = res
+        _F[name] = f
+    return f
 
 
 def _ptr(x):
@@ -120,22 +150,22 @@ def _opts(o):
 
 def _mk(t):
     def trsm(m, n, alpha, A, lda, B, ldb, stream=None):
-        return _F["hsma_trsm_" + t](m, n, _scalar(t, alpha), _ptr(A), lda, _ptr(B), ldb, _stream(stream))
+        return _fn("hsma_trsm_" + t)(m, n, _scalar(t, alpha), _ptr(A), lda, _ptr(B), ldb, _stream(stream))
 
     def strided_batched(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch_count, stream=None):
-        return _F["hsma_trsm_strided_batched_" + t](m, n, _scalar(t, alpha), _ptr(A), lda, strideA,
-                                                   _ptr(B), ldb, strideB, batch_count, _stream(stream))
+        return _fn("hsma_trsm_strided_batched_" + t)(m, n, _scalar(t, alpha), _ptr(A), lda, strideA,
+                                                     _ptr(B), ldb, strideB, batch_count, _stream(stream))
 
     def ex(m, n, alpha, A, lda, B, ldb, opts=None, stream=None):
-        return _F["hsma_trsm_ex_" + t](m, n, _scalar(t, alpha), _ptr(A), lda, _ptr(B), ldb,
-                                      _opts(opts), _stream(stream))
+        return _fn("hsma_trsm_ex_" + t)(m, n, _scalar(t, alpha), _ptr(A), lda, _ptr(B), ldb,
+                                        _opts(opts), _stream(stream))
 
     def diag_inv(m, nb, ib, A, lda, invA, stream=None):
-        return _F["hsma_diag_inv_" + t](m, nb, ib, _ptr(A), lda, _ptr(invA), _stream(stream))
+        return _fn("hsma_diag_inv_" + t)(m, nb, ib, _ptr(A), lda, _ptr(invA), _stream(stream))
 
     def gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower=0, stream=None):
-        return _F["hsma_gemm_" + t](M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta),
-                                   _ptr(C), ldc, int(a_lower), _stream(stream))
+        return _fn("hsma_gemm_" + t)(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta),
+                                     _ptr(C), ldc, int(a_lower), _stream(stream))
 
     return trsm, strided_batched, ex, diag_inv, gemm
 
@@ -148,16 +178,16 @@ def _mk(t):
 
 def hsma_solve_tri_f32(n, k, A, B, X, ne02, ne03, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3,
                        stream=None):
-    return _F["hsma_solve_tri_f32"](n, k, _ptr(A), _ptr(B), _ptr(X), ne02, ne03, sA1, sA2, sA3,
-                                    sB1, sB2, sB3, sX1, sX2, sX3, _stream(stream))
+    return _fn("hsma_solve_tri_f32")(n, k, _ptr(A), _ptr(B), _ptr(X), ne02, ne03, sA1, sA2, sA3,
+                                     sB1, sB2, sB3, sX1, sX2, sX3, _stream(stream))
 
 
 def hsma_trsm_block_size(dtype, m):
-    return _F["hsma_trsm_block_size"](dtype, m)
+    return _fn("hsma_trsm_block_size")(dtype, m)
 
 
 def hsma_status_string(status):
-    return _F["hsma_status_string"](status).decode()
+    return _fn("hsma_status_string")(status).decode()
 
 
 status_string = hsma_status_string

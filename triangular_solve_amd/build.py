@@ -21,8 +21,19 @@ FLAGS = [
 ]
 
 
-def _compile(src):
+def _deps_mtime():
+    """Newest modification time of the headers every source includes."""
+    hdrs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".inc"))]
+    hdrs.append(os.path.join(ROOT, "include", "hsma_trsm.h"))
+    return max(os.path.getmtime(h) for h in hdrs)
+
+
+def _compile(src, incremental=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        newest = max(os.path.getmtime(os.path.join(CSRC, src)), _deps_mtime())
+        if os.path.getmtime(obj) > newest:
+            return obj, []
     cmd = ["hipcc"] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -31,10 +42,12 @@ def _compile(src):
     return obj, warn
 
 
-def build(verbose=False):
+def build(verbose=False, incremental=False):
+    """Compile every source (incremental: only those older than their
+    source or a shared header) and link the library in-tree."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda f: _compile(f, incremental), SOURCES))
     objs = [o for o, _ in results]
     if verbose:
         for _, w in results:
@@ -50,4 +63,4 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

@@ -58,6 +58,10 @@ hipError_t device_pool(int dev, hipMemPool_t *out)
 
 hipError_t workspace_alloc(void **p, size_t bytes, hipStream_t s)
 {
+    // Allocation-failure injection for tests of the error path: read on
+    // every call, before any HIP call.
+    const char *fail = std::getenv("HSMA_TEST_FAIL_ALLOC");
+    if (fail && fail[0] == '1' && fail[1] == 0) return hipErrorOutOfMemory;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -154,7 +158,10 @@ inline c64 from_abi(hsma_double_complex v) { return {v.re, v.im}; }
 
 hsma_status hip_status(hipError_t e)
 {
-    return e == hipSuccess ? HSMA_STATUS_SUCCESS : HSMA_STATUS_HIP_ERROR;
+    if (e == hipSuccess) return HSMA_STATUS_SUCCESS;
+    // Only workspace allocations report out-of-memory.
+    if (e == hipErrorOutOfMemory) return HSMA_STATUS_ALLOC_FAILED;
+    return HSMA_STATUS_HIP_ERROR;
 }
 
 int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
@@ -171,6 +178,9 @@ hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
         if (o->ib < 1) return HSMA_STATUS_INVALID_VALUE;
         if (nb != 0 && (nb % o->ib != 0 || nb / o->ib > 64)) return HSMA_STATUS_INVALID_VALUE;
     }
+    if (o->n_events < 0) return HSMA_STATUS_INVALID_VALUE;
+    if (o->n_events > 0 && (!o->events || !o->event_phase || !o->events_used))
+        return HSMA_STATUS_INVALID_POINTER;
     return HSMA_STATUS_SUCCESS;
 }
 
@@ -235,6 +245,8 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     if (batch > 1 && strideB < ldb * n) return HSMA_STATUS_INVALID_SIZE;
     const hsma_status os = check_opts(opts, dt, m);
     if (os != HSMA_STATUS_SUCCESS) return os;
+    const bool timed = opts && opts->n_events > 0;
+    if (timed) *opts->events_used = 0;
     if (m == 0 || n == 0 || batch == 0) return HSMA_STATUS_SUCCESS;
     if (!B) return HSMA_STATUS_INVALID_POINTER;
     hipStream_t s = (hipStream_t)stream;
@@ -256,6 +268,19 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     int ib = (opts && opts->ib) ? opts->ib : (nb / 8 > 0 ? nb / 8 : 1);
     if (nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
 
+    // Phase events (single problems only: the *_ex entry points).
+    PhaseRec rec;
+    if (timed) {
+        const int need = blocked_phase_events((m + nb - 1) / nb) + (is_one(alpha) ? 0 : 1);
+        if (batch != 1 || opts->n_events < need) {
+            *opts->events_used = need;
+            return HSMA_STATUS_INVALID_VALUE;
+        }
+        rec.ev = (hipEvent_t *)opts->events;
+        rec.phase = opts->event_phase;
+        rec.cap = opts->n_events;
+    }
+
     const int64_t welems = blocked_workspace_elems(m, n, nb);
     void *work = nullptr;
     if (workspace_alloc(&work, (size_t)welems * sizeof(T), s) != hipSuccess || !work) {
@@ -263,9 +288,14 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
         return HSMA_STATUS_ALLOC_FAILED;
     }
     hipError_t e = hipSuccess;
-    if (!is_one(alpha)) e = scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, false, s);
+    if (!is_one(alpha)) {
+        if (timed) e = rec.mark(HSMA_PHASE_SCALE, s);
+        if (e == hipSuccess) e = scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, false, s);
+    }
     for (int64_t b = 0; b < batch && e == hipSuccess; ++b)
-        e = blocked_solve<T>(m, n, nb, ib, A + b * strideA, lda, B + b * strideB, ldb, (T *)work, s);
+        e = blocked_solve<T>(m, n, nb, ib, A + b * strideA, lda, B + b * strideB, ldb, (T *)work, s,
+                             timed ? &rec : nullptr);
+    if (timed) *opts->events_used = rec.used;
     const hipError_t ef = workspace_free(work, s);
     if (e != hipSuccess || ef != hipSuccess) return HSMA_STATUS_HIP_ERROR;
     return HSMA_STATUS_SUCCESS;

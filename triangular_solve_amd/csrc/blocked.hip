@@ -21,6 +21,7 @@
 //    [[re, -im], [im, re]], so one complex multiply-add costs exactly the four
 //    real ones the flop count assumes.
 //  * copy_kernel - places the solved block row W into B.
+#include "../../include/hsma_trsm.h"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -108,10 +109,17 @@ __global__ void __launch_bounds__(256) diag_inv_kernel(const T *__restrict__ A, 
             T y[G];
 #pragma unroll
             for (int c = 0; c < G; ++c) y[c] = ybuf[k & 1][c];
+            // only the rows below k change: row k and the rows above keep
+            // their values also when y is inf or NaN (a zero pivot)
 #pragma unroll
-            for (int q = 0; q < R; ++q)
+            for (int q = 0; q < R; ++q) {
+                const bool below = tid * R + q > k;
 #pragma unroll
-                for (int c = 0; c < G; ++c) w[q][c] = fms(w[q][c], dcur[q][kk], y[c]);
+                for (int c = 0; c < G; ++c) {
+                    const T u = fms(w[q][c], dcur[q][kk], y[c]);
+                    w[q][c] = below ? u : w[q][c];
+                }
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < CK; ++kk)
@@ -713,19 +721,25 @@ int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
 
 template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
-                         int64_t ldb, T *work, hipStream_t s)
+                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec)
 {
     using R = typename traits<T>::real;
     const int64_t nt = (m + nb - 1) / nb;
     T *invA = work;
     T *W = work + nt * nb * nb;
-    hipError_t e = blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, W, s)
-                                                     : diag_invert<T>(m, nb, ib, A, lda, invA, s);
+    auto mark = [&](int ph) { return rec ? rec->mark(ph, s) : hipSuccess; };
+    hipError_t e = mark(HSMA_PHASE_DIAG_INV);
+    if (e == hipSuccess)
+        e = blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, W, s)
+                                              : diag_invert<T>(m, nb, ib, A, lda, invA, s);
     for (int64_t t = 0; t < nt && e == hipSuccess; ++t) {
         const int64_t r0 = t * nb;
         const int64_t rb = m - r0 < nb ? m - r0 : nb;
         // X_t = D_t^{-1} B_t (D_t^{-1} is lower triangular: upper tiles skipped)
-        e = gemm<T>(rb, n, rb, R(1), invA + t * nb * nb, nb, B + r0, ldb, R(0), W, nb, true, s);
+        e = mark(HSMA_PHASE_INV_GEMM);
+        if (e == hipSuccess)
+            e = gemm<T>(rb, n, rb, R(1), invA + t * nb * nb, nb, B + r0, ldb, R(0), W, nb, true, s);
+        if (e == hipSuccess) e = mark(HSMA_PHASE_COPY);
         if (e != hipSuccess) break;
         for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += 65535) {
             const int64_t nc = n - c0 < 65535 ? n - c0 : 65535;
@@ -735,10 +749,14 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
         }
         if (e != hipSuccess) break;
         // B[below] -= A[below, t] X_t
-        if (r0 + rb < m)
-            e = gemm<T>(m - r0 - rb, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb, R(1),
-                        B + r0 + rb, ldb, false, s);
+        if (r0 + rb < m) {
+            e = mark(HSMA_PHASE_TRAILING);
+            if (e == hipSuccess)
+                e = gemm<T>(m - r0 - rb, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb, R(1),
+                            B + r0 + rb, ldb, false, s);
+        }
     }
+    if (e == hipSuccess) e = mark(HSMA_PHASE_END);
     return e;
 }
 
@@ -753,7 +771,7 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
                                         typename traits<T>::real, T *, int64_t, int64_t, int64_t, \
                                         hipStream_t);                                             \
     template hipError_t blocked_solve<T>(int64_t, int64_t, int, int, const T *, int64_t, T *,     \
-                                         int64_t, T *, hipStream_t);
+                                         int64_t, T *, hipStream_t, PhaseRec *);
 HSMA_INST(float)
 HSMA_INST(double)
 HSMA_INST(c32)

@@ -84,23 +84,22 @@ __device__ inline cplx<R> fms(cplx<R> w, cplx<R> a, cplx<R> x)
     return r;
 }
 
-// 1/d with IEEE division (complex: conj(d) / |d|^2).
+// 1/d with IEEE division. Complex d by Smith's method: with p the part of
+// larger magnitude and q the other, r = q/p and t = 1/(p + q r); then
+// 1/d = (t, -r t) when p = re, (r t, -t) when p = im. Nothing is squared,
+// so no intermediate over- or underflows where 1/d is representable (the
+// plain conj(d)/|d|^2 loses half of the exponent range). d = 0 gives NaN.
 __device__ inline float recip(float d) { return 1.0f / d; }
 __device__ inline double recip(double d) { return 1.0 / d; }
 template <typename R>
 __device__ inline cplx<R> recip(cplx<R> d)
 {
-    const R den = d.re * d.re + d.im * d.im;
-    return {d.re / den, -d.im / den};
-}
-
-inline float host_recip(float a) { return 1.0f / a; }
-inline double host_recip(double a) { return 1.0 / a; }
-template <typename R>
-inline cplx<R> host_recip(cplx<R> d)
-{
-    const R den = d.re * d.re + d.im * d.im;
-    return {d.re / den, -d.im / den};
+    const bool sw = __builtin_fabs(d.im) > __builtin_fabs(d.re);
+    const R p = sw ? d.im : d.re, q = sw ? d.re : d.im;
+    const R r = q / p;
+    const R t = R(1) / fmaR(q, r, p);
+    const R u = r * t;
+    return sw ? cplx<R>{u, -t} : cplx<R>{t, -u};
 }
 
 // ---- cross-lane broadcast of a wave-uniform lane index (v_readlane) --------

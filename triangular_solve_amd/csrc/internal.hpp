@@ -40,7 +40,8 @@ hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB
                         T alpha, bool set_zero, hipStream_t s);
 
 // Stream-ordered workspace from the library's memory pool of the current
-// device (created on first use; freed memory is kept for reuse).
+// device (created on first use; freed memory is kept for reuse). Returns
+// hipErrorOutOfMemory without any HIP call when HSMA_TEST_FAIL_ALLOC=1.
 hipError_t workspace_alloc(void **p, size_t bytes, hipStream_t s);
 hipError_t workspace_free(void *p, hipStream_t s);
 
@@ -70,11 +71,31 @@ hipError_t gemm_strided(int64_t M, int64_t N, int64_t K, typename traits<T>::rea
                         int64_t strideB, typename traits<T>::real beta, T *C, int64_t ldc,
                         int64_t strideC, int64_t batch, hipStream_t s);
 
+// Phase events of the blocked path: mark(phase) records the caller's next
+// event on the stream and notes which phase starts there.
+struct PhaseRec {
+    hipEvent_t *ev = nullptr;
+    int32_t *phase = nullptr;
+    int cap = 0;
+    int used = 0;
+    hipError_t mark(int ph, hipStream_t s)
+    {
+        if (used >= cap) return hipErrorInvalidValue;
+        phase[used] = ph;
+        return hipEventRecord(ev[used++], s);
+    }
+};
+// Events a blocked solve with nt diagonal blocks records (excluding scaling):
+// inversion, then per block row the inverse multiply, the copy and (all but
+// the last) the trailing update, then the end.
+inline int blocked_phase_events(int64_t nt) { return (int)(3 * nt + 1); }
+
 // Whole blocked solve of one problem (B already scaled by alpha), with a
 // caller-provided workspace of blocked_workspace_elems(m, n, nb) elements.
+// rec (nullable) records the phase events.
 int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb);
 template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
-                         int64_t ldb, T *work, hipStream_t s);
+                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec = nullptr);
 
 }  // namespace hsma

@@ -62,14 +62,22 @@ __global__ void __launch_bounds__(64) update_kernel(const float *__restrict__ A,
 }
 
 // Forward substitution of one wave's 64 rows (lane = row), coefficients
-// a[j] = a_ij / a_ii below the diagonal and 0 elsewhere, w = b / a_ii.
+// a[j] = a_ij / a_ii below the diagonal and 0 elsewhere, w = b / a_ii. Step j
+// updates only the rows below j, so finished rows keep their values even
+// when a later x_j is inf or NaN.
 template <int KW>
 __device__ __forceinline__ void wave_substitute(const float (&a)[64], float (&w)[KW])
 {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
+    for (int j = 0; j < 64; ++j) {
+        const bool below = j < lane;
 #pragma unroll
-        for (int q = 0; q < KW; ++q) w[q] = __builtin_fmaf(-a[j], readlane(w[q], j), w[q]);
+        for (int q = 0; q < KW; ++q) {
+            const float u = __builtin_fmaf(-a[j], readlane(w[q], j), w[q]);
+            w[q] = below ? u : w[q];
+        }
+    }
 }
 
 // 64 < n <= 128 in one launch: two waves per (problem, group of KW columns),

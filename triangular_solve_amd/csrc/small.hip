@@ -99,10 +99,17 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
         }
 #pragma unroll
         for (int j = 0; j < 64; ++j) a[j] = j < lane ? mul(a[j], inv) : zero_of(T());
+        // Step j updates only the rows below j: a finished row keeps its
+        // value even when a later x_j is inf or NaN (0 * inf would be NaN).
 #pragma unroll
-        for (int j = 0; j < 64; ++j)
+        for (int j = 0; j < 64; ++j) {
+            const bool below = j < lane;
 #pragma unroll
-            for (int q = 0; q < KW; ++q) w[q] = fms(w[q], a[j], readlane(w[q], j));
+            for (int q = 0; q < KW; ++q) {
+                const T u = fms(w[q], a[j], readlane(w[q], j));
+                w[q] = below ? u : w[q];
+            }
+        }
 #pragma unroll
         for (int q = 0; q < KW; ++q) {
             const int c = c0 + q;
@@ -140,13 +147,15 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
 
     // Forward substitution. After step j-1, lane j holds the finished x_j;
     // every lane below subtracts its (scaled) a_ij * x_j. Lanes at or above
-    // j read a zero coefficient and keep their value.
+    // j keep their value (also when x_j is inf or NaN).
     auto step = [&](int j) {
         const T a = AT[j * kLdsStride + lane];
+        const bool below = j < lane;
 #pragma unroll
         for (int q = 0; q < KW; ++q) {
             const T x = readlane(w[q], j);
-            w[q] = fms(w[q], a, x);
+            const T u = fms(w[q], a, x);
+            w[q] = below ? u : w[q];
         }
     };
     if (m == 64) {
@@ -273,6 +282,17 @@ __device__ __forceinline__ T ld_uniform(cptr<T> p, int idx)
 typedef int v4i __attribute__((ext_vector_type(4)));
 using lptr = __attribute__((address_space(3))) char *;
 using lptr_v4i = __attribute__((address_space(3))) v4i *;
+
+// Orders this wave's LDS accesses before and after the call: lanes exchange
+// data through the wave's own tile, and the fences keep the compiler from
+// moving an access across the exchange (one wave's LDS operations complete
+// in issue order, so no wait is needed in hardware).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Per-wave LDS tile of 64 columns x one 128-byte line; the 16-byte pad of
 // the column stride keeps both the line-wise and the column-wise 16-byte
@@ -445,16 +465,16 @@ struct PanelState {
     int lane128;  // lane * 128: this lane's line of a prefetched segment
     int tv[64];   // results of the segments' prefetch loads, retired later
     T myinv;      // 1/a_ll of this lane's row index l
-    T alpha_inv;
 };
 
-// Rows [r0, r0 + P) of the wave's columns into st.w, lane = column. Each
-// 128-byte line of a column is fetched by 8 lanes with 16-byte loads (a
+// alpha * rows [r0, r0 + P) of the wave's columns into st.w, lane = column.
+// Each 128-byte line of a column is fetched by 8 lanes with 16-byte loads (a
 // lane-per-column load would touch 64 lines per instruction), written to
 // the tile and read back one column per lane. The next tile's loads are in
 // flight while the current one is transposed.
 template <typename T, int P>
-__device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int r0)
+__device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int r0, T alpha,
+                                           bool scale)
 {
     constexpr int V = 16 / (int)sizeof(T);
     constexpr int L = 128 / (int)sizeof(T);
@@ -481,6 +501,7 @@ __device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             *(lptr_v4i)(st.tile + (q * 8 + (lane >> 3)) * kTileCol + sub * 16) = cur[q];
+        wave_lds_sync();
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const v4i v = *(const lptr_v4i)(st.tile + lane * kTileCol + k * 16);
@@ -489,17 +510,25 @@ __device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int
 #pragma unroll
             for (int e = 0; e < V; ++e) st.w[ch * L + k * V + e] = t[e];
         }
+        wave_lds_sync();
         if (ch + 1 < NCH) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
         }
     }
+    // alpha applied on the way in, so the solve and every stored row of X
+    // are in the units of X (a later panel reads finished rows back as they
+    // are)
+    if (scale) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) st.w[e] = mul(alpha, st.w[e]);
+    }
 }
 
-// alpha * st.w into rows [r0, r0 + P) of the wave's columns, the reverse
-// of load_panel (columns past ncol are not written).
+// st.w into rows [r0, r0 + P) of the wave's columns, the reverse of
+// load_panel (columns past ncol are not written).
 template <typename T, int P>
-__device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, int r0, T alpha)
+__device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, int r0)
 {
     constexpr int V = 16 / (int)sizeof(T);
     constexpr int L = 128 / (int)sizeof(T);
@@ -512,17 +541,19 @@ __device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, in
         for (int k = 0; k < 8; ++k) {
             T t[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) t[e] = mul(alpha, st.w[ch * L + k * V + e]);
+            for (int e = 0; e < V; ++e) t[e] = st.w[ch * L + k * V + e];
             v4i v;
             __builtin_memcpy(&v, t, 16);
             *(lptr_v4i)(st.tile + lane * kTileCol + k * 16) = v;
         }
+        wave_lds_sync();
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int col = q * 8 + (lane >> 3);
             const v4i v = *(const lptr_v4i)(st.tile + col * kTileCol + sub * 16);
             if (col < st.ncol) *(gptr<v4i>)(bw + col * st.ldb + r0 + ch * L + sub * V) = v;
         }
+        wave_lds_sync();
     }
 }
 
@@ -542,6 +573,10 @@ __device__ __forceinline__ void reload_fill(PanelState<T, P> &st, int k0)
     const int a = lane >> 3, b = lane & 7;
     const int r = (a + b) & 7;
     const gptr<T> bw = global_after(st.Bw, st.x);
+    // every earlier read of the tile has returned before the loads below
+    // overwrite it
+    wave_lds_sync();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         int col = q * 8 + b;
@@ -550,6 +585,7 @@ __device__ __forceinline__ void reload_fill(PanelState<T, P> &st, int k0)
                                          (__attribute__((address_space(3))) void *)(st.tile + q * 1024), 16, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
+    wave_lds_sync();
 }
 
 // x of row k0 + k (k < 8) of this lane's column from the tile reload_fill wrote.
@@ -593,7 +629,7 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
                 // the tile: one line of rows per refill for all the wave's
                 // columns, then one LDS read per segment
                 if constexpr (pc.col % 8 == 0) reload_fill<T, P>(st, pc.col);
-                st.x = mul(reload_x<T, P>(st, pc.col % 8), st.alpha_inv);
+                st.x = reload_x<T, P>(st, pc.col % 8);
             } else if constexpr (pc.diag) {
                 constexpr int j = pc.col - R0;
                 if constexpr (std::is_same<T, float>::value) {
@@ -608,6 +644,10 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
                     r = __builtin_fma(r, e, r);
                     e = __builtin_fma(-dv, r, 1.0);
                     r = __builtin_fma(r, e, r);
+                    // IEEE special cases of 1/dv (zero, infinite or NaN pivot,
+                    // overflowing reciprocal), which the Newton steps turn
+                    // into NaN
+                    r = __builtin_amdgcn_div_fixup(r, dv, 1.0);
                     st.x = st.w[j] * r;
                 }
                 st.w[j] = st.x;
@@ -683,22 +723,20 @@ __device__ __forceinline__ void run_batches(PanelState<T, P> &st)
 }
 
 template <typename T, int P, int NPANEL, int PI>
-__device__ __forceinline__ void run_panels(PanelState<T, P> &st, T alpha,
+__device__ __forceinline__ void run_panels(PanelState<T, P> &st, T alpha, bool scale,
                                            typename traits<T>::real wlast)
 {
     if constexpr (PI < NPANEL) {
         constexpr int r0 = PI * P;
         // a later panel's rows are loaded only after the earlier panel is done
         const gptr<T> bw = global_after(st.Bw, wlast);
-        load_panel<T, P>(st, bw, r0);
+        load_panel<T, P>(st, bw, r0, alpha, scale);
         st.x = zero_of(T());
         run_batches<T, P, r0, kBatch<T>, kAhead<T>, 0>(st);
-        // The solve ran on B itself; alpha is applied to X on the way out
-        // (A (alpha^{-1} X) = B has the same substitution with alpha factored out).
-        store_panel<T, P>(st, bw, r0, alpha);
+        store_panel<T, P>(st, bw, r0);
         typename traits<T>::real wl;
         if constexpr (traits<T>::is_complex) wl = st.w[P - 1].re; else wl = st.w[P - 1];
-        run_panels<T, P, NPANEL, PI + 1>(st, alpha, wl);
+        run_panels<T, P, NPANEL, PI + 1>(st, alpha, scale, wl);
     }
 }
 
@@ -707,7 +745,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
                                                          int64_t strideA, T *__restrict__ B,
                                                          int64_t ldb, int64_t strideB, int64_t n,
                                                          int64_t nchunks, int64_t items, T alpha,
-                                                         T alpha_inv, int64_t per, int64_t strideA2,
+                                                         int scale, int64_t per, int64_t strideA2,
                                                          int64_t strideB2)
 {
     extern __shared__ __attribute__((aligned(16))) char colane_lds[];
@@ -736,11 +774,10 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     st.ldb = ldb;
     st.ncol = (int)(n - cfirst < 64 ? n - cfirst : 64);
     st.tile = (lptr)colane_lds + wave * kTileBytes;
-    st.alpha_inv = alpha_inv;
 
     st.lane128 = lane * 128;
     if constexpr (!kDiagInStream<T>) st.myinv = recip(Ap[lane + lane * lda]);
-    run_panels<T, P, NPANEL, 0>(st, alpha, typename traits<T>::real(0));
+    run_panels<T, P, NPANEL, 0>(st, alpha, scale != 0, typename traits<T>::real(0));
 }
 
 // Compute units of the current device (cached per device).
@@ -782,8 +819,6 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
     // 4096 problems (re-read rows had been evicted from L2 and came back
     // from HBM).
     constexpr int NP = sizeof(T) == 16 ? 2 : 1;
-    // Earlier panels' rows are read back from B already scaled by alpha.
-    const T alpha_inv = host_recip(alpha);
     // The 16-byte tile accesses need 16-byte aligned columns.
     if (((uintptr_t)B & 15) != 0 || ((ldb * (int64_t)sizeof(T)) & 15) != 0 ||
         ((strideB * (int64_t)sizeof(T)) & 15) != 0 || ((strideB2 * (int64_t)sizeof(T)) & 15) != 0)
@@ -799,7 +834,7 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
         if (share > lds) lds = share;
     }
     hipLaunchKernelGGL((colane_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), lds, s, A, lda,
-                       strideA, B, ldb, strideB, n, nchunks, items, alpha, alpha_inv, per, strideA2,
+                       strideA, B, ldb, strideB, n, nchunks, items, alpha, is_one(alpha) ? 0 : 1, per, strideA2,
                        strideB2);
     return hipGetLastError();
 }
