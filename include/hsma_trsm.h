@@ -62,6 +62,7 @@ typedef int hsma_status;
 #define HSMA_STATUS_ALLOC_FAILED 4    /* workspace allocation failed */
 #define HSMA_STATUS_HIP_ERROR 5       /* a HIP runtime call or kernel launch failed */
 #define HSMA_STATUS_INVALID_VALUE 6   /* bad option value */
+#define HSMA_STATUS_SCRATCH_TOO_SMALL 7 /* hsma_trsm_noalloc: problem exceeds its fixed scratch */
 
 typedef struct { float re, im; } hsma_float_complex;
 typedef struct { double re, im; } hsma_double_complex;
@@ -265,6 +266,30 @@ hsma_status hsma_gemm_z(int64_t M, int64_t N, int64_t K, double alpha,
                         const hsma_double_complex *A, int64_t lda, const hsma_double_complex *B,
                         int64_t ldb, double beta, hsma_double_complex *C, int64_t ldc,
                         int32_t a_lower, void *stream);
+
+/*
+ * hsma_trsm_noalloc: the solve of hsma_trsm_{s,d,c,z} (same operation,
+ * layout and semantics; dtype is an HSMA_DTYPE_* code and alpha points to
+ * one host value of that element type) without any device allocation, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. It calls no hipMalloc, hipFree or
+ * other allocating routine. The blocked path's workspace comes from a fixed
+ * 64 MiB device array in the library, one per GPU, held from the library's
+ * first use on that GPU until the process ends. The block size is the
+ * table's, halved until the inverted diagonal blocks fill at most half of
+ * it, and B is solved in column chunks that fit the rest (so large problems
+ * may run with a smaller N_B than hsma_trsm_*). Limit: roughly
+ * 16 * m * sizeof(element) <= 32 MiB, i.e. m <= 524288 (f32), 262144 (f64,
+ * c64), 131072 (c128); larger m returns SCRATCH_TOO_SMALL before any GPU
+ * work. m <= 64 uses no scratch. All calls on one GPU share its array:
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race and must be serialised by the caller; the array keeps the last
+ * call's contents, and nothing in it needs to start at zero.
+ * Errors: INVALID_SIZE, INVALID_POINTER (alpha NULL, or A/B NULL as for
+ * hsma_trsm_*), INVALID_VALUE (bad dtype), SCRATCH_TOO_SMALL, HIP_ERROR.
+ */
+hsma_status hsma_trsm_noalloc(int32_t dtype, int64_t m, int64_t n, const void *alpha,
+                              const void *A, int64_t lda, void *B, int64_t ldb, void *stream);
 
 /*
  * hsma_trsm_block_size: the outer block size N_B the blocked path uses for

@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(hs):
     lib = ctypes.CDLL(hs.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(names) == hs.EXPORTS
@@ -151,3 +151,20 @@ def test_phase_event_checks(hs):
     assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, bad, 0) == hs.INVALID_POINTER
     neg = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, -1, None, None, None)
     assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, neg, 0) == hs.INVALID_VALUE
+
+
+def test_noalloc_checks(hs, monkeypatch):
+    """hsma_trsm_noalloc validates arguments and rejects problems beyond its
+    scratch before any GPU work."""
+    f = hs.hsma_trsm_noalloc
+    assert f(7, 10, 10, 1.0, BAD, 10, BAD, 10, 0) == hs.INVALID_VALUE
+    assert f(1, -1, 10, 1.0, BAD, 10, BAD, 10, 0) == hs.INVALID_SIZE
+    assert f(1, 10, 10, 1.0, BAD, 9, BAD, 10, 0) == hs.INVALID_SIZE
+    assert f(1, 0, 10, 1.0, None, 1, None, 1, 0) == hs.SUCCESS
+    assert f(1, 10, 10, 1.0, BAD, 10, None, 10, 0) == hs.INVALID_POINTER
+    # 16 * m * 8 bytes > 32 MiB
+    assert f(1, 1 << 19, 4, 1.0, BAD, 1 << 19, BAD, 1 << 19, 0) == hs.SCRATCH_TOO_SMALL
+    assert f(3, 200000, 4, 1.0, BAD, 200000, BAD, 200000, 0) == hs.SCRATCH_TOO_SMALL
+    monkeypatch.setenv("HSMA_NOALLOC_LIMIT", "4096")
+    assert f(0, 100, 4, 1.0, BAD, 100, BAD, 100, 0) == hs.SCRATCH_TOO_SMALL
+    assert hs.hsma_status_string(hs.SCRATCH_TOO_SMALL) == "problem exceeds the no-allocation scratch"

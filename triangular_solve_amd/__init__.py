@@ -25,6 +25,7 @@ NOT_SUPPORTED = 3
 ALLOC_FAILED = 4
 HIP_ERROR = 5
 INVALID_VALUE = 6
+SCRATCH_TOO_SMALL = 7
 
 DTYPE_F32, DTYPE_F64, DTYPE_C64, DTYPE_C128 = 0, 1, 2, 3
 PATH_AUTO, PATH_SMALL, PATH_BLOCKED = 0, 1, 2
@@ -75,6 +76,7 @@ for _t in "sdcz":
 _PROTO["hsma_solve_tri_f32"] = ([_i64, _i64, _p, _p, _p] + [_i64] * 11 + [_p], ctypes.c_int)
 _PROTO["hsma_trsm_block_size"] = ([_i32, _i64], ctypes.c_int32)
 _PROTO["hsma_status_string"] = ([ctypes.c_int], ctypes.c_char_p)
+_PROTO["hsma_trsm_noalloc"] = ([_i32, _i64, _i64, _p, _p, _i64, _p, _i64, _p], ctypes.c_int)
 
 EXPORTS = sorted(_PROTO)
 
@@ -180,6 +182,24 @@ def hsma_solve_tri_f32(n, k, A, B, X, ne02, ne03, sA1, sA2, sA3, sB1, sB2, sB3, 
                        stream=None):
     return _fn("hsma_solve_tri_f32")(n, k, _ptr(A), _ptr(B), _ptr(X), ne02, ne03, sA1, sA2, sA3,
                                      sB1, sB2, sB3, sX1, sX2, sX3, _stream(stream))
+
+
+_CTYPE_OF_CODE = {DTYPE_F32: ctypes.c_float, DTYPE_F64: ctypes.c_double, DTYPE_C64: FloatComplex,
+                  DTYPE_C128: DoubleComplex}
+
+
+def hsma_trsm_noalloc(dtype, m, n, alpha, A, lda, B, ldb, stream=None):
+    """dtype is a DTYPE_* code; alpha a Python number (passed by address)."""
+    ct = _CTYPE_OF_CODE.get(dtype)
+    if ct is None:
+        a = ctypes.c_double(0.0)
+    elif dtype in (DTYPE_C64, DTYPE_C128):
+        v = complex(alpha)
+        a = ct(v.real, v.imag)
+    else:
+        a = ct(float(alpha))
+    return _fn("hsma_trsm_noalloc")(dtype, m, n, ctypes.byref(a), _ptr(A), lda, _ptr(B), ldb,
+                                    _stream(stream))
 
 
 def hsma_trsm_block_size(dtype, m):

@@ -138,6 +138,8 @@ int env_nb()
 }
 
 
+}  // namespace
+
 int choose_nb(int dtype, int64_t m)
 {
     int nb = env_nb();
@@ -148,6 +150,8 @@ int choose_nb(int dtype, int64_t m)
     if (nb > cap) nb = (int)(cap < 16 ? 16 : cap);
     return nb;
 }
+
+namespace {
 
 // ---------------------------------------------------------------------------
 
@@ -182,23 +186,6 @@ hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
     if (o->n_events > 0 && (!o->events || !o->event_phase || !o->events_used))
         return HSMA_STATUS_INVALID_POINTER;
     return HSMA_STATUS_SUCCESS;
-}
-
-// Small path on column-major storage, in place.
-template <typename T>
-hipError_t small_path(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
-                      T *B, int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s)
-{
-    // The lane-per-column kernel needs the full 64 rows, enough columns to
-    // fill a wavefront and 16-byte aligned columns of B; otherwise the
-    // lane-per-row kernel.
-    const int64_t sb = batch > 1 ? strideB : 0;
-    const bool aligned = ((uintptr_t)B & 15) == 0 && ((ldb * (int64_t)sizeof(T)) & 15) == 0 &&
-                         ((sb * (int64_t)sizeof(T)) & 15) == 0;
-    if (m == 64 && n >= 32 && aligned)
-        return small_colane<T>(n, alpha, A, lda, strideA, B, ldb, sb, batch, s);
-    return small_rowlane<T>(A, 1, lda, strideA, 0, B, 1, ldb, strideB, 0, B, 1, ldb, strideB, 0,
-                            m, n, batch, 1, alpha, s);
 }
 
 // Batches of 64 < m <= 256: block rows of 64 for the whole batch at once
@@ -516,6 +503,7 @@ const char *hsma_status_string(hsma_status status)
     case HSMA_STATUS_ALLOC_FAILED: return "workspace allocation failed";
     case HSMA_STATUS_HIP_ERROR: return "HIP error";
     case HSMA_STATUS_INVALID_VALUE: return "invalid value";
+    case HSMA_STATUS_SCRATCH_TOO_SMALL: return "problem exceeds the no-allocation scratch";
     default: return "unknown status";
     }
 }

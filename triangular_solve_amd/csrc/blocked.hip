@@ -161,8 +161,6 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
                                   hipStream_t s);
 template <typename T>
 static bool blocked_inverse_applies(int64_t m, int nb);
-int64_t blocked_inverse_temp_elems(int64_t m, int nb);
-
 // Inversion of all diagonal blocks: the blocked-inverse formula where it
 // applies (temporaries allocated stream-ordered), else diag_inv_kernel.
 template <typename T>
@@ -720,18 +718,21 @@ int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
 }
 
 template <typename T>
-hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
-                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec)
+hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
+                          hipStream_t s)
+{
+    return blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, temp, s)
+                                             : diag_invert<T>(m, nb, ib, A, lda, invA, s);
+}
+
+template <typename T>
+hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
+                         T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec)
 {
     using R = typename traits<T>::real;
     const int64_t nt = (m + nb - 1) / nb;
-    T *invA = work;
-    T *W = work + nt * nb * nb;
     auto mark = [&](int ph) { return rec ? rec->mark(ph, s) : hipSuccess; };
-    hipError_t e = mark(HSMA_PHASE_DIAG_INV);
-    if (e == hipSuccess)
-        e = blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, W, s)
-                                              : diag_invert<T>(m, nb, ib, A, lda, invA, s);
+    hipError_t e = hipSuccess;
     for (int64_t t = 0; t < nt && e == hipSuccess; ++t) {
         const int64_t r0 = t * nb;
         const int64_t rb = m - r0 < nb ? m - r0 : nb;
@@ -760,6 +761,19 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     return e;
 }
 
+template <typename T>
+hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
+                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec)
+{
+    const int64_t nt = (m + nb - 1) / nb;
+    T *invA = work;
+    T *W = work + nt * nb * nb;   // also the inversion's temporary, before W is used
+    hipError_t e = rec ? rec->mark(HSMA_PHASE_DIAG_INV, s) : hipSuccess;
+    if (e == hipSuccess) e = blocked_invert<T>(m, nb, ib, A, lda, invA, W, s);
+    if (e == hipSuccess) e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec);
+    return e;
+}
+
 #define HSMA_INST(T)                                                                              \
     template hipError_t diag_invert<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t);  \
     template hipError_t diag_invert_any<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t); \
@@ -771,6 +785,10 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
                                         typename traits<T>::real, T *, int64_t, int64_t, int64_t, \
                                         hipStream_t);                                             \
     template hipError_t blocked_solve<T>(int64_t, int64_t, int, int, const T *, int64_t, T *,     \
+                                         int64_t, T *, hipStream_t, PhaseRec *);                  \
+    template hipError_t blocked_invert<T>(int64_t, int, int, const T *, int64_t, T *, T *,        \
+                                          hipStream_t);                                           \
+    template hipError_t blocked_apply<T>(int64_t, int64_t, int, const T *, int64_t, const T *, T *, \
                                          int64_t, T *, hipStream_t, PhaseRec *);
 HSMA_INST(float)
 HSMA_INST(double)

@@ -98,4 +98,37 @@ template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
                          int64_t ldb, T *work, hipStream_t s, PhaseRec *rec = nullptr);
 
+// The two halves of blocked_solve. blocked_invert: all diagonal blocks into
+// invA (ceil(m/nb) blocks of nb x nb), using temp (blocked_inverse_temp_elems
+// elements) for the blocked-inverse merges. blocked_apply: the block-row
+// loop for n columns of B with the inverted blocks, W holding nb x n.
+int64_t blocked_inverse_temp_elems(int64_t m, int nb);
+template <typename T>
+hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
+                          hipStream_t s);
+template <typename T>
+hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
+                         T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec = nullptr);
+
+// Small-regime dispatch on column-major storage, in place (m <= 64): the
+// lane-per-column kernel needs the full 64 rows, enough columns to fill a
+// wavefront and 16-byte aligned columns of B; otherwise the lane-per-row
+// kernel.
+template <typename T>
+hipError_t small_path(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
+                      T *B, int64_t ldb, int64_t strideB, int64_t batch, hipStream_t s)
+{
+    const int64_t sb = batch > 1 ? strideB : 0;
+    const bool aligned = ((uintptr_t)B & 15) == 0 && ((ldb * (int64_t)sizeof(T)) & 15) == 0 &&
+                         ((sb * (int64_t)sizeof(T)) & 15) == 0;
+    if (m == 64 && n >= 32 && aligned)
+        return small_colane<T>(n, alpha, A, lda, strideA, B, ldb, sb, batch, s);
+    return small_rowlane<T>(A, 1, lda, strideA, 0, B, 1, ldb, strideB, 0, B, 1, ldb, strideB, 0,
+                            m, n, batch, 1, alpha, s);
+}
+
+// Outer block size for an m x m problem of the given dtype code: the table
+// by nearest size, or the HSMA_NB override (api.cpp).
+int choose_nb(int dtype, int64_t m);
+
 }  // namespace hsma
