@@ -48,6 +48,9 @@ def _get():
         lib.oracle_trsm.restype = i
         lib.oracle_gemm.argtypes = [i, i64, i64, i64, p, i64, i64, p, i64, i64, p]
         lib.oracle_gemm.restype = i
+        lib.oracle_trsm_general.argtypes = [i, i, i, i, i, i64, i64, i64, p, p, i64, i64, i64,
+                                            p, i64, i64, i64, p, i]
+        lib.oracle_trsm_general.restype = i
         _lib = lib
     return _lib
 
@@ -98,6 +101,50 @@ def trsm(A, B, alpha=1.0, threads=None):
                             X.ctypes.data, threads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_trsm failed")
+    return X.transpose(0, 2, 1)
+
+
+SIDE = {"L": 0, "R": 1}
+UPLO = {"L": 0, "U": 1}
+TRANS = {"N": 0, "T": 1, "C": 2}
+DIAG = {"N": 0, "U": 1}
+
+
+def trsm_general(A, B, side="L", uplo="L", trans="N", diag="N", alpha=1.0, threads=None):
+    """One TRSM variant per problem, in double precision (see oracle.c):
+    side "L": op(A) X = alpha B; side "R": X op(A) = alpha B; op = "N", "T" or
+    "C" (conjugate transpose); uplo "L"/"U" says which triangle of A is used
+    (the other is never read); diag "U": unit diagonal (never read).
+
+    A: (batch, k, k) array view, [b, i, j] = element (i, j), k = m for the left
+       side and n for the right side (any strides).
+    B: (batch, m, n) array view, [b, i, c] = element (i, c).
+    Returns X as (batch, m, n) float64 / complex128.
+    """
+    A = np.asarray(A)
+    B = np.asarray(B)
+    if A.ndim == 2:
+        return trsm_general(A[None], B[None], side, uplo, trans, diag, alpha, threads)[0]
+    dt = _dtype_of(A)
+    if _dtype_of(B) != dt:
+        raise TypeError("A and B dtypes differ")
+    batch, k, k2 = A.shape
+    b2, m, n = B.shape
+    if k != k2 or b2 != batch or k != (m if side == "L" else n):
+        raise ValueError("shape mismatch")
+    sab, sai, saj = _strides(A)
+    sbb, sbi, sbj = _strides(B)
+    if batch == 1:
+        sab = sbb = 0
+    cp = dt in COMPLEX
+    X = np.empty((batch, n, m), dtype=np.complex128 if cp else np.float64)
+    al = np.array([complex(alpha).real, complex(alpha).imag], dtype=np.float64)
+    rc = _get().oracle_trsm_general(CODE[dt], SIDE[side], UPLO[uplo], TRANS[trans], DIAG[diag],
+                                    m, n, batch, al.ctypes.data, A.ctypes.data, sai, saj, sab,
+                                    B.ctypes.data, sbi, sbj, sbb, X.ctypes.data,
+                                    threads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_trsm_general failed")
     return X.transpose(0, 2, 1)
 
 

@@ -213,3 +213,167 @@ int oracle_gemm(int dtype, int64_t M, int64_t N, int64_t K,
         }
     return 0;
 }
+
+/*
+ * The other TRSM variants (side, triangle, transpose, unit diagonal), by
+ * definition. The HSMA-TRSM pages evaluate only the left-side lower case and
+ * leave "other TRSM variants" open (news summary, "A result tied to a narrow
+ * benchmark"); the variants here are the usual BLAS ones:
+ *
+ *   side left:   op(A) X = alpha B,  A is m x m
+ *   side right:  X op(A) = alpha B,  A is n x n
+ *   op(A) = A (trans 0), A^T (trans 1) or A^H (trans 2, conjugate transpose);
+ *   uplo 0: A lower triangular, 1: upper (the other triangle is never read);
+ *   diag 1: unit diagonal, op(A)(i, i) = 1 and the stored diagonal is never read.
+ *
+ * Each system is solved by substitution in the order its triangle allows:
+ * left side, op(A) lower: x_i = (alpha b_i - sum_{j<i} op(A)(i,j) x_j) / op(A)(i,i)
+ * for i = 0, 1, ...; op(A) upper: the same with j > i for i = m-1, m-2, ...
+ * Right side, row r of B: sum_k x_k op(A)(k, j) = alpha b_j, so op(A) upper
+ * gives x_j = (alpha b_j - sum_{k<j} x_k op(A)(k,j)) / op(A)(j,j) for
+ * j = 0, 1, ..., and op(A) lower the same with k > j, j descending. Sums run
+ * over the already solved unknowns in the order they were solved. Complex
+ * products and the textbook complex division in double, as above.
+ *
+ * X is written in double, column-major m x n per problem (leading dimension
+ * m), problems back to back, as for oracle_trsm.
+ */
+typedef struct {
+    int dtype, side, uplo, trans, diag;
+    int64_t m, n, k; /* k = order of A: m (left) or n (right) */
+    double ar, ai;
+    const void *A; int64_t sai, saj, sab;
+    const void *B; int64_t sbi, sbj, sbb;
+    double *X;
+    int64_t lo, hi; /* range of (problem * vectors + vector) items */
+} general_job;
+
+/* op(A)(i, j) of problem b as a (re, im) pair. */
+static void op_a(const general_job *J, int64_t b, int64_t i, int64_t j, double *re, double *im)
+{
+    if (J->diag == 1 && i == j) { *re = 1.0; *im = 0.0; return; }
+    const int64_t r = J->trans ? j : i;   /* element of the stored A */
+    const int64_t c = J->trans ? i : j;
+    get(J->dtype, J->A, b * J->sab + r * J->sai + c * J->saj, re, im);
+    if (J->trans == 2) *im = -*im;
+}
+
+/* (pr, pi) = (ar, ai) * (br, bi) */
+static void cprod(double ar, double ai, double br, double bi, double *pr, double *pi)
+{
+    *pr = ar * br - ai * bi;
+    *pi = ar * bi + ai * br;
+}
+
+/* One right-hand-side vector: column c (left side) or row c (right side). */
+static void solve_vector(const general_job *J, int64_t b, int64_t c, double *x)
+{
+    const int left = J->side == 0;
+    const int64_t k = J->k;
+    /* op(A) lower iff (A lower and not transposed) or (A upper and transposed) */
+    const int op_lower = (J->uplo == 0) == (J->trans == 0);
+    /* substitution runs forward when the unknown of step s only needs earlier ones */
+    const int forward = left ? op_lower : !op_lower;
+    for (int64_t s = 0; s < k; ++s) {
+        const int64_t i = forward ? s : k - 1 - s;
+        double br, bi;
+        const int64_t row = left ? i : c, col = left ? c : i;
+        get(J->dtype, J->B, b * J->sbb + row * J->sbi + col * J->sbj, &br, &bi);
+        double accr, acci;
+        cprod(J->ar, cplx_of(J->dtype) ? J->ai : 0.0, br, bi, &accr, &acci);
+        for (int64_t t = 0; t < s; ++t) {
+            const int64_t j = forward ? t : k - 1 - t;   /* solved unknowns, in solve order */
+            double opr, opi, pr, pi;
+            if (left) op_a(J, b, i, j, &opr, &opi);      /* op(A)(i, j) x_j */
+            else op_a(J, b, j, i, &opr, &opi);           /* x_j op(A)(j, i) */
+            cprod(opr, opi, x[2 * j], x[2 * j + 1], &pr, &pi);
+            accr -= pr;
+            acci -= pi;
+        }
+        double dr, di;
+        op_a(J, b, i, i, &dr, &di);
+        if (cplx_of(J->dtype)) {
+            const double den = dr * dr + di * di;
+            x[2 * i] = (accr * dr + acci * di) / den;
+            x[2 * i + 1] = (acci * dr - accr * di) / den;
+        } else {
+            x[2 * i] = accr / dr;
+            x[2 * i + 1] = 0.0;
+        }
+    }
+    /* store: X(row, col) of problem b, column-major with leading dimension m */
+    const int cp = cplx_of(J->dtype);
+    double *Xb = J->X + b * J->m * J->n * (cp ? 2 : 1);
+    for (int64_t i = 0; i < k; ++i) {
+        const int64_t row = left ? i : c, col = left ? c : i;
+        const int64_t at = row + col * J->m;
+        if (cp) { Xb[2 * at] = x[2 * i]; Xb[2 * at + 1] = x[2 * i + 1]; }
+        else Xb[at] = x[2 * i];
+    }
+}
+
+static void *general_run(void *arg)
+{
+    const general_job *J = (const general_job *)arg;
+    double *x = (double *)malloc(sizeof(double) * 2 * (size_t)(J->k > 0 ? J->k : 1));
+    if (!x) return (void *)1;
+    const int64_t per = J->side == 0 ? J->n : J->m;
+    for (int64_t it = J->lo; it < J->hi; ++it) solve_vector(J, it / per, it % per, x);
+    free(x);
+    return 0;
+}
+
+/*
+ * Solve batch problems of one variant (codes above). A: element (i, j) of
+ * problem b at A[b*sab + i*sai + j*saj], order m (left) or n (right); B and
+ * X as for oracle_trsm. Returns 0, or -1 on a bad argument or allocation
+ * failure. Bitwise independent of the thread count.
+ */
+int oracle_trsm_general(int dtype, int side, int uplo, int trans, int diag, int64_t m, int64_t n,
+                        int64_t batch, const double *alpha,
+                        const void *A, int64_t sai, int64_t saj, int64_t sab,
+                        const void *B, int64_t sbi, int64_t sbj, int64_t sbb,
+                        double *X, int nthreads)
+{
+    if (dtype < 0 || dtype > 3 || side < 0 || side > 1 || uplo < 0 || uplo > 1 || trans < 0 ||
+        trans > 2 || diag < 0 || diag > 1 || m < 0 || n < 0 || batch < 0 || !alpha)
+        return -1;
+    const int64_t per = side == 0 ? n : m;
+    const int64_t items = batch * per;
+    if (m == 0 || n == 0 || items == 0) return 0;
+    if (!A || !B || !X) return -1;
+    general_job base;
+    memset(&base, 0, sizeof base);
+    base.dtype = dtype; base.side = side; base.uplo = uplo; base.trans = trans; base.diag = diag;
+    base.m = m; base.n = n; base.k = side == 0 ? m : n;
+    base.ar = alpha[0]; base.ai = cplx_of(dtype) ? alpha[1] : 0.0;
+    base.A = A; base.sai = sai; base.saj = saj; base.sab = sab;
+    base.B = B; base.sbi = sbi; base.sbj = sbj; base.sbb = sbb;
+    base.X = X;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (items < nthreads) nthreads = (int)items;
+    general_job *jobs = (general_job *)malloc(sizeof(general_job) * (size_t)nthreads);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int *started = (int *)calloc((size_t)nthreads, sizeof(int));
+    if (!jobs || !th || !started) { free(jobs); free(th); free(started); return -1; }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = base;
+        jobs[t].lo = items * t / nthreads;
+        jobs[t].hi = items * (t + 1) / nthreads;
+    }
+    int bad = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], 0, general_run, &jobs[t]) == 0) started[t] = 1;
+        else bad = 1;
+    }
+    if (general_run(&jobs[0])) bad = 1;
+    for (int t = 1; t < nthreads; ++t) {
+        if (!started[t]) continue;
+        void *r = 0;
+        pthread_join(th[t], &r);
+        if (r) bad = 1;
+    }
+    free(jobs); free(th); free(started);
+    return bad ? -1 : 0;
+}
