@@ -203,7 +203,7 @@ def phase_split(hs, torch, f, m, dt, dA, dB, nbu, stream):
     handles = (ctypes.c_void_p * cap)(*[e.cuda_event for e in evs])
     phases = (ctypes.c_int32 * cap)()
     used = ctypes.c_int32(0)
-    opts = hs.TrsmOpts(nbu, 0, hs.PATH_BLOCKED, cap, handles, phases, ctypes.pointer(used))
+    opts = hs.TrsmOpts(nbu, 0, hs.PATH_BLOCKED, 0, cap, handles, phases, ctypes.pointer(used))
     hs.check(f(m, m, 1.0, dA, m, dB, m, opts, stream), "trsm_ex_" + dt + " (timed phases)")
     torch.cuda.synchronize()
     out = {name: 0.0 for name in hs.PHASE_NAMES.values()}

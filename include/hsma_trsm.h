@@ -125,6 +125,84 @@ hsma_status hsma_trsm_strided_batched_z(int64_t m, int64_t n, hsma_double_comple
                                         int64_t batch_count, void *stream);
 
 /*
+ * hsma_trsm_general_{s,d,c,z} and hsma_trsm_strided_batched_general_{s,d,c,z}:
+ * the other TRSM variants, which the HSMA-TRSM pages leave untested (news
+ * summary, "A result tied to a narrow benchmark": nonsquare shapes and
+ * other TRSM variants remain unresolved), with the usual BLAS meaning:
+ *   side HSMA_SIDE_LEFT:   op(A) X = alpha B,  A is m x m
+ *   side HSMA_SIDE_RIGHT:  X op(A) = alpha B,  A is n x n
+ *   uplo HSMA_FILL_LOWER / HSMA_FILL_UPPER: the triangle of A that is used
+ *        (the other one is never read)
+ *   trans HSMA_OP_N: op(A) = A; HSMA_OP_T: A^T; HSMA_OP_C: A^H (conjugate
+ *        transpose; the same as HSMA_OP_T for real types)
+ *   diag HSMA_DIAG_UNIT: a unit diagonal is assumed and the stored diagonal
+ *        is never read; HSMA_DIAG_NON_UNIT: the stored diagonal is used
+ * B is m x n with ldb >= max(1, m); lda >= max(1, order of A). X overwrites
+ * B; m != n is allowed everywhere. side LEFT, uplo LOWER, trans N, diag
+ * NON_UNIT is exactly hsma_trsm_* (hsma_trsm_strided_batched_*).
+ * Every variant is solved as the canonical left-side lower-triangular
+ * system C Y = alpha Bhat, with C = op(A) (left) or op(A)^T (right), taken
+ * in reverse index order when it is upper triangular, and Bhat = B or B^T
+ * (rows reversed with C). For an order of at most 64 the small regime
+ * reads these as strided views (lane-per-row kernel); batches of order
+ * 64 < k <= 256 gather the triangles and right-hand sides of the whole batch
+ * into workspace and run in block rows of 64; larger orders gather one
+ * problem at a time and run the blocked solver on the copy, then X is
+ * scattered back. The gathers take workspace (k*k, plus m*n unless Bhat is
+ * B itself); ALLOC_FAILED if it cannot be had.
+ * Errors: INVALID_VALUE (bad side/uplo/trans/diag code), INVALID_SIZE,
+ *         INVALID_POINTER, ALLOC_FAILED, HIP_ERROR.
+ */
+#define HSMA_SIDE_LEFT 0
+#define HSMA_SIDE_RIGHT 1
+#define HSMA_FILL_LOWER 0
+#define HSMA_FILL_UPPER 1
+#define HSMA_OP_N 0
+#define HSMA_OP_T 1
+#define HSMA_OP_C 2
+#define HSMA_DIAG_NON_UNIT 0
+#define HSMA_DIAG_UNIT 1
+
+hsma_status hsma_trsm_general_s(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, float alpha, const float *A, int64_t lda,
+                                float *B, int64_t ldb, void *stream);
+hsma_status hsma_trsm_general_d(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, double alpha, const double *A, int64_t lda,
+                                double *B, int64_t ldb, void *stream);
+hsma_status hsma_trsm_general_c(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, hsma_float_complex alpha,
+                                const hsma_float_complex *A, int64_t lda, hsma_float_complex *B,
+                                int64_t ldb, void *stream);
+hsma_status hsma_trsm_general_z(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, hsma_double_complex alpha,
+                                const hsma_double_complex *A, int64_t lda, hsma_double_complex *B,
+                                int64_t ldb, void *stream);
+hsma_status hsma_trsm_strided_batched_general_s(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n, float alpha,
+                                                const float *A, int64_t lda, int64_t strideA,
+                                                float *B, int64_t ldb, int64_t strideB,
+                                                int64_t batch_count, void *stream);
+hsma_status hsma_trsm_strided_batched_general_d(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n, double alpha,
+                                                const double *A, int64_t lda, int64_t strideA,
+                                                double *B, int64_t ldb, int64_t strideB,
+                                                int64_t batch_count, void *stream);
+hsma_status hsma_trsm_strided_batched_general_c(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n,
+                                                hsma_float_complex alpha,
+                                                const hsma_float_complex *A, int64_t lda,
+                                                int64_t strideA, hsma_float_complex *B,
+                                                int64_t ldb, int64_t strideB, int64_t batch_count,
+                                                void *stream);
+hsma_status hsma_trsm_strided_batched_general_z(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n,
+                                                hsma_double_complex alpha,
+                                                const hsma_double_complex *A, int64_t lda,
+                                                int64_t strideA, hsma_double_complex *B,
+                                                int64_t ldb, int64_t strideB, int64_t batch_count,
+                                                void *stream);
+
+/*
  * hsma_solve_tri_f32: the ggml SOLVE_TRI operation (llama.cpp PR #17457,
  * "SOLVE_TRI CUDA kernel for small matrices"): for every batch index
  * (i2, i3) in [0, ne02) x [0, ne03), solve A X = B with A n x n lower
@@ -168,6 +246,20 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
  *         solver's size) and ignores ib.
  *   path  HSMA_PATH_AUTO, HSMA_PATH_SMALL (requires m <= 64) or
  *         HSMA_PATH_BLOCKED (any m >= 1)
+ *   inv   route of the diagonal-block inversion (blocked path):
+ *         HSMA_INV_AUTO: BLOCKED where it applies, else COLUMN;
+ *         HSMA_INV_BLOCKED: 64 x 64 sub-blocks by substitution against
+ *           identity columns, merged by the block-inverse formula in batched
+ *           matrix-core products (m a multiple of nb, nb a multiple of 64,
+ *           nb >= 128);
+ *         HSMA_INV_FUSED: the "traditional" fused kernel the paper's
+ *           blocked section describes and replaces: each 2*ib x 2*ib
+ *           diagonal block inverted whole in LDS (4*ib^2 elements), then the
+ *           same merges up to nb (ib 32 or 64, 32 for double complex; m a
+ *           multiple of nb, nb a multiple of 2*ib); an A/B alternative;
+ *         HSMA_INV_COLUMN: column-level substitution against identity
+ *           tiles (nb <= 1024).
+ *         A route that does not apply to (m, nb, ib) gives INVALID_VALUE.
  *   Timing of the blocked path's phases (the paper's Table 3 splits the
  *   run time into diagonal inversion and GEMM update): when n_events > 0,
  *   events[0 .. n_events) are hipEvent_t handles created by the caller, and
@@ -186,6 +278,10 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
 #define HSMA_PATH_AUTO 0
 #define HSMA_PATH_SMALL 1
 #define HSMA_PATH_BLOCKED 2
+#define HSMA_INV_AUTO 0
+#define HSMA_INV_BLOCKED 1
+#define HSMA_INV_FUSED 2
+#define HSMA_INV_COLUMN 3
 #define HSMA_PHASE_END (-1)
 #define HSMA_PHASE_SCALE 0      /* B := alpha * B */
 #define HSMA_PHASE_DIAG_INV 1   /* inversion of all diagonal blocks */
@@ -196,6 +292,7 @@ typedef struct {
     int32_t nb;
     int32_t ib;
     int32_t path;
+    int32_t inv;
     int32_t n_events;
     void **events;
     int32_t *event_phase;
@@ -243,6 +340,23 @@ hsma_status hsma_diag_inv_c(int64_t m, int32_t nb, int32_t ib, const hsma_float_
                             int64_t lda, hsma_float_complex *invA, void *stream);
 hsma_status hsma_diag_inv_z(int64_t m, int32_t nb, int32_t ib, const hsma_double_complex *A,
                             int64_t lda, hsma_double_complex *invA, void *stream);
+
+/*
+ * hsma_diag_inv_ex_{s,d,c,z}: hsma_diag_inv_* with the block size, inner
+ * block and inversion route taken from opts (nb, ib, inv; NULL = defaults;
+ * path and the event fields are ignored), for checking each route on its
+ * own. Errors as hsma_diag_inv_*; INVALID_VALUE if the route does not apply.
+ */
+hsma_status hsma_diag_inv_ex_s(int64_t m, const hsma_trsm_opts *opts, const float *A, int64_t lda,
+                               float *invA, void *stream);
+hsma_status hsma_diag_inv_ex_d(int64_t m, const hsma_trsm_opts *opts, const double *A,
+                               int64_t lda, double *invA, void *stream);
+hsma_status hsma_diag_inv_ex_c(int64_t m, const hsma_trsm_opts *opts,
+                               const hsma_float_complex *A, int64_t lda,
+                               hsma_float_complex *invA, void *stream);
+hsma_status hsma_diag_inv_ex_z(int64_t m, const hsma_trsm_opts *opts,
+                               const hsma_double_complex *A, int64_t lda,
+                               hsma_double_complex *invA, void *stream);
 
 /*
  * hsma_gemm_{s,d,c,z}: C = beta*C + alpha*A*B with A M x K, B K x N,
@@ -293,13 +407,15 @@ hsma_status hsma_trsm_noalloc(int32_t dtype, int64_t m, int64_t n, const void *a
 
 /*
  * hsma_trsm_block_size: the outer block size N_B the blocked path uses for
- * an m x m problem of the given dtype (HSMA_DTYPE_*), from the built-in
- * "size x dtype -> block" table by nearest tested size (HSMA-TRSM paper,
- * adaptive blocking section). Returns 0 for m <= 64 (small path) and -1 for
- * a bad dtype. The environment variable HSMA_NB, read once, overrides the
- * table when set to a valid block size.
+ * an m x m system with n right-hand sides of the given dtype (HSMA_DTYPE_*),
+ * from the built-in "scale x dtype -> block" table (HSMA-TRSM paper,
+ * adaptive blocking section), here keyed on the shape (m, n): the nearest
+ * tested shape by |log2 m - log2 m_i| + |log2 n - log2 n_i|. Returns 0 for
+ * m <= 64 (small path) and -1 for a bad dtype; n < 1 counts as 1. The
+ * environment variable HSMA_NB, read once, overrides the table when set to
+ * a valid block size.
  */
-int32_t hsma_trsm_block_size(int32_t dtype, int64_t m);
+int32_t hsma_trsm_block_size(int32_t dtype, int64_t m, int64_t n);
 
 /* Static, human-readable name of a status code. */
 const char *hsma_status_string(hsma_status status);

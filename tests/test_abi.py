@@ -25,7 +25,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(hs):
     lib = ctypes.CDLL(hs.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 36
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(names) == hs.EXPORTS
@@ -109,15 +109,48 @@ def test_gemm_and_diag_inv_checks(hs):
     assert d(0, 128, 16, None, 1, None, 0) == hs.SUCCESS
 
 
+def nb_table():
+    """The built-in N_B table as {dtype code: [(m, n, nb), ...]}."""
+    text = open(os.path.join(ROOT, "triangular_solve_amd", "csrc", "nb_table.inc")).read()
+    out = {}
+    for code, name in enumerate(["kNbF32", "kNbF64", "kNbC64", "kNbC128"]):
+        body = re.search(r"static const NbEntry %s\[\] = \{(.*)\};" % name, text).group(1)
+        out[code] = [tuple(int(v) for v in t) for t in re.findall(r"\{(\d+), (\d+), (\d+)\}", body)]
+    return out
+
+
+def expected_nb(entries, code, m, n):
+    """The lookup rule: nearest tested shape by |log2 m - log2 m_i| + |log2 n - log2 n_i|
+    (first entry on ties), halved until blocks above 1024 rows (512 for c128)
+    divide m, clamped to m rounded up to a multiple of 16."""
+    import math
+    best, bd = None, 1e300
+    for (mi, ni, nb) in entries:
+        d = abs(math.log2(m) - math.log2(mi)) + abs(math.log2(max(n, 1)) - math.log2(ni))
+        if d < bd - 1e-12:
+            best, bd = nb, d
+    nb = best
+    while not (nb <= (512 if code == 3 else 1024) or m % nb == 0):
+        nb //= 2
+    cap = (m + 15) // 16 * 16
+    return min(nb, max(cap, 16))
+
+
 def test_block_size_table(hs):
+    tab = nb_table()
     for code in range(4):
-        assert hs.hsma_trsm_block_size(code, 64) == 0
-        for m in (65, 100, 1000, 1024, 3000, 8192, 16384, 50000):
-            nb = hs.hsma_trsm_block_size(code, m)
-            assert nb % 16 == 0 and 16 <= nb <= 2048
-            assert nb <= ((m + 15) // 16) * 16
-            assert nb <= (512 if code == 3 else 1024) or m % nb == 0
-    assert hs.hsma_trsm_block_size(7, 100) == -1
+        assert hs.hsma_trsm_block_size(code, 64, 64) == 0
+        assert len({(m, n) for m, n, _ in tab[code]}) == len(tab[code]) > 5
+        for (m, n, nb) in tab[code]:       # every tested shape returns its own entry
+            assert hs.hsma_trsm_block_size(code, m, n) == expected_nb(tab[code], code, m, n) == nb
+        for m in (65, 100, 1000, 1024, 3000, 8192, 12000, 16384, 50000):
+            for n in (1, 8, 64, 100, 700, 5000, 16384, 100000):
+                nb = hs.hsma_trsm_block_size(code, m, n)
+                assert nb == expected_nb(tab[code], code, m, n), (code, m, n)
+                assert nb % 16 == 0 and 16 <= nb <= 2048
+                assert nb <= ((m + 15) // 16) * 16
+                assert nb <= (512 if code == 3 else 1024) or m % nb == 0
+    assert hs.hsma_trsm_block_size(7, 100, 100) == -1
 
 
 @pytest.mark.parametrize("t", ["f32", "f64", "c64", "c128"])
@@ -141,15 +174,15 @@ def test_phase_event_checks(hs):
     used = ctypes.c_int32(-5)
     phases = (ctypes.c_int32 * 4)()
     evs = (ctypes.c_void_p * 4)()
-    o = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 4, evs, phases, ctypes.pointer(used))
+    o = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 0, 4, evs, phases, ctypes.pointer(used))
     # m = 1000, nb = 128: 8 diagonal blocks -> 3*8 + 1 events (+1 with alpha != 1)
     assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, o, 0) == hs.INVALID_VALUE
     assert used.value == 25
     assert hs.entry("ex", "f64")(1000, 4, 2, BAD, 1000, BAD, 1000, o, 0) == hs.INVALID_VALUE
     assert used.value == 26
-    bad = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 4, evs, None, ctypes.pointer(used))
+    bad = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 0, 4, evs, None, ctypes.pointer(used))
     assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, bad, 0) == hs.INVALID_POINTER
-    neg = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, -1, None, None, None)
+    neg = hs.TrsmOpts(128, 0, hs.PATH_BLOCKED, 0, -1, None, None, None)
     assert hs.entry("ex", "f64")(1000, 4, 1, BAD, 1000, BAD, 1000, neg, 0) == hs.INVALID_VALUE
 
 

@@ -173,7 +173,7 @@ def test_phase_events(hs, dt, m, nb, alpha):
     handles = (ctypes.c_void_p * cap)(*[ev.cuda_event for ev in evs])
     phases = (ctypes.c_int32 * cap)()
     used = ctypes.c_int32(0)
-    o = hs.TrsmOpts(nb, 0, hs.PATH_BLOCKED, cap, handles, phases, ctypes.pointer(used))
+    o = hs.TrsmOpts(nb, 0, hs.PATH_BLOCKED, 0, cap, handles, phases, ctypes.pointer(used))
     hs.check(f(m, n, alpha, dA, m, dB2, m, o, stream), "timed")
     torch.cuda.synchronize()
     assert used.value == need

@@ -28,7 +28,12 @@ INVALID_VALUE = 6
 SCRATCH_TOO_SMALL = 7
 
 DTYPE_F32, DTYPE_F64, DTYPE_C64, DTYPE_C128 = 0, 1, 2, 3
+SIDE = {"L": 0, "R": 1}
+UPLO = {"L": 0, "U": 1}
+OP = {"N": 0, "T": 1, "C": 2}
+DIAG = {"N": 0, "U": 1}
 PATH_AUTO, PATH_SMALL, PATH_BLOCKED = 0, 1, 2
+INV_AUTO, INV_BLOCKED, INV_FUSED, INV_COLUMN = 0, 1, 2, 3
 
 # Phase codes of the blocked path's timing events (hsma_trsm_opts.events).
 PHASE_END, PHASE_SCALE, PHASE_DIAG_INV, PHASE_INV_GEMM, PHASE_COPY, PHASE_TRAILING = -1, 0, 1, 2, 3, 4
@@ -46,7 +51,7 @@ class DoubleComplex(ctypes.Structure):
 
 class TrsmOpts(ctypes.Structure):
     _fields_ = [("nb", ctypes.c_int32), ("ib", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("n_events", ctypes.c_int32), ("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("inv", ctypes.c_int32), ("n_events", ctypes.c_int32), ("events", ctypes.POINTER(ctypes.c_void_p)),
                 ("event_phase", ctypes.POINTER(ctypes.c_int32)),
                 ("events_used", ctypes.POINTER(ctypes.c_int32))]
 
@@ -71,10 +76,17 @@ for _t in "sdcz":
     _PROTO["hsma_trsm_ex_" + _t] = (
         [_i64, _i64, S, _p, _i64, _p, _i64, ctypes.POINTER(TrsmOpts), _p], ctypes.c_int)
     _PROTO["hsma_diag_inv_" + _t] = ([_i64, _i32, _i32, _p, _i64, _p, _p], ctypes.c_int)
+    _PROTO["hsma_diag_inv_ex_" + _t] = ([_i64, ctypes.POINTER(TrsmOpts), _p, _i64, _p, _p], ctypes.c_int)
     _PROTO["hsma_gemm_" + _t] = (
         [_i64, _i64, _i64, Rl, _p, _i64, _p, _i64, Rl, _p, _i64, _i32, _p], ctypes.c_int)
+for _t in "sdcz":
+    S = _SCAL[_t]
+    _PROTO["hsma_trsm_general_" + _t] = (
+        [_i32, _i32, _i32, _i32, _i64, _i64, S, _p, _i64, _p, _i64, _p], ctypes.c_int)
+    _PROTO["hsma_trsm_strided_batched_general_" + _t] = (
+        [_i32, _i32, _i32, _i32, _i64, _i64, S, _p, _i64, _i64, _p, _i64, _i64, _i64, _p], ctypes.c_int)
 _PROTO["hsma_solve_tri_f32"] = ([_i64, _i64, _p, _p, _p] + [_i64] * 11 + [_p], ctypes.c_int)
-_PROTO["hsma_trsm_block_size"] = ([_i32, _i64], ctypes.c_int32)
+_PROTO["hsma_trsm_block_size"] = ([_i32, _i64, _i64], ctypes.c_int32)
 _PROTO["hsma_status_string"] = ([ctypes.c_int], ctypes.c_char_p)
 _PROTO["hsma_trsm_noalloc"] = ([_i32, _i64, _i64, _p, _p, _i64, _p, _i64, _p], ctypes.c_int)
 
@@ -147,7 +159,8 @@ def _opts(o):
         return None
     if isinstance(o, TrsmOpts):
         return ctypes.byref(o)
-    return ctypes.byref(TrsmOpts(int(o.get("nb", 0)), int(o.get("ib", 0)), int(o.get("path", 0))))
+    return ctypes.byref(TrsmOpts(int(o.get("nb", 0)), int(o.get("ib", 0)), int(o.get("path", 0)),
+                                 int(o.get("inv", 0))))
 
 
 def _mk(t):
@@ -169,6 +182,22 @@ def _mk(t):
         return _fn("hsma_gemm_" + t)(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta),
                                      _ptr(C), ldc, int(a_lower), _stream(stream))
 
+    def general(side, uplo, trans, diag, m, n, alpha, A, lda, B, ldb, stream=None):
+        return _fn("hsma_trsm_general_" + t)(side, uplo, trans, diag, m, n, _scalar(t, alpha), _ptr(A),
+                                             lda, _ptr(B), ldb, _stream(stream))
+
+    def strided_batched_general(side, uplo, trans, diag, m, n, alpha, A, lda, strideA, B, ldb,
+                                strideB, batch_count, stream=None):
+        return _fn("hsma_trsm_strided_batched_general_" + t)(
+            side, uplo, trans, diag, m, n, _scalar(t, alpha), _ptr(A), lda, strideA, _ptr(B), ldb,
+            strideB, batch_count, _stream(stream))
+
+    def diag_inv_ex(m, opts, A, lda, invA, stream=None):
+        return _fn("hsma_diag_inv_ex_" + t)(m, _opts(opts), _ptr(A), lda, _ptr(invA), _stream(stream))
+
+    globals()["hsma_diag_inv_ex_" + t] = diag_inv_ex
+    globals()["hsma_trsm_general_" + t] = general
+    globals()["hsma_trsm_strided_batched_general_" + t] = strided_batched_general
     return trsm, strided_batched, ex, diag_inv, gemm
 
 
@@ -202,8 +231,8 @@ def hsma_trsm_noalloc(dtype, m, n, alpha, A, lda, B, ldb, stream=None):
                                     _stream(stream))
 
 
-def hsma_trsm_block_size(dtype, m):
-    return _fn("hsma_trsm_block_size")(dtype, m)
+def hsma_trsm_block_size(dtype, m, n=None):
+    return _fn("hsma_trsm_block_size")(dtype, m, m if n is None else n)
 
 
 def hsma_status_string(status):
@@ -220,7 +249,9 @@ DTYPE_CODE = {"f32": DTYPE_F32, "f64": DTYPE_F64, "c64": DTYPE_C64, "c128": DTYP
 def entry(kind, dtype):
     """The binding function of one entry point, e.g. entry("trsm", "c64") -> hsma_trsm_c."""
     names = {"trsm": "hsma_trsm_%s", "strided_batched": "hsma_trsm_strided_batched_%s",
-             "ex": "hsma_trsm_ex_%s", "diag_inv": "hsma_diag_inv_%s", "gemm": "hsma_gemm_%s"}
+             "ex": "hsma_trsm_ex_%s", "diag_inv": "hsma_diag_inv_%s", "gemm": "hsma_gemm_%s",
+             "general": "hsma_trsm_general_%s", "diag_inv_ex": "hsma_diag_inv_ex_%s",
+             "strided_batched_general": "hsma_trsm_strided_batched_general_%s"}
     return globals()[names[kind] % LETTER[dtype]]
 
 

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhsma_trsm.so")
-SOURCES = ["api.cpp", "small.hip", "blocked.hip", "medium.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "small.hip", "blocked.hip", "medium.hip", "noalloc.hip", "variants.hip"]
 ARCH = os.environ.get("HSMA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

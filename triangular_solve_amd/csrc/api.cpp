@@ -12,7 +12,7 @@
 #include <cstdlib>
 #include <mutex>
 
-#include "../../include/hsma_trsm.h"
+#include "hsma_trsm.h"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -76,18 +76,20 @@ hipError_t workspace_free(void *p, hipStream_t s) { return hipFreeAsync(p, s); }
 namespace {
 
 // ---------------------------------------------------------------------------
-// Block-size table: tested sizes m_i and the best N_B at each, per dtype.
-// Lookup takes the tested size nearest to m on a log scale (ties go to the
-// smaller size), then clamps N_B to m rounded up to a multiple of 16.
+// Block-size table: tested shapes (m_i, n_i) and the best N_B at each, per
+// dtype. Lookup takes the tested shape nearest to (m, n) by
+// |log2 m - log2 m_i| + |log2 n - log2 n_i| (ties go to the earlier entry,
+// which the table lists by increasing m, then n), then clamps N_B to m
+// rounded up to a multiple of 16.
 
 struct NbEntry {
-    int64_t m;
+    int64_t m, n;
     int nb;
 };
 
 #include "nb_table.inc"
 
-int table_lookup(int dtype, int64_t m)
+int table_lookup(int dtype, int64_t m, int64_t n)
 {
     const NbEntry *tab = nullptr;
     int len = 0;
@@ -98,11 +100,12 @@ int table_lookup(int dtype, int64_t m)
     case 3: tab = kNbC128; len = (int)(sizeof(kNbC128) / sizeof(kNbC128[0])); break;
     default: return -1;
     }
-    const double lm = std::log2((double)m);
+    const double lm = std::log2((double)m), ln = std::log2((double)(n > 0 ? n : 1));
     int best = 0;
     double bd = 1e300;
     for (int i = 0; i < len; ++i) {
-        const double d = std::fabs(lm - std::log2((double)tab[i].m));
+        const double d = std::fabs(lm - std::log2((double)tab[i].m)) +
+                         std::fabs(ln - std::log2((double)tab[i].n));
         if (d < bd - 1e-12) { bd = d; best = i; }
     }
     return tab[best].nb;
@@ -140,10 +143,10 @@ int env_nb()
 
 }  // namespace
 
-int choose_nb(int dtype, int64_t m)
+int choose_nb(int dtype, int64_t m, int64_t n)
 {
     int nb = env_nb();
-    if (nb <= 0) nb = table_lookup(dtype, m);
+    if (nb <= 0) nb = table_lookup(dtype, m, n);
     if (nb > kMaxNb) nb = kMaxNb;
     while (!nb_fits(nb, m, dtype)) nb /= 2;
     const int64_t cap = ((m + 15) / 16) * 16;
@@ -174,6 +177,7 @@ hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
 {
     if (!o) return HSMA_STATUS_SUCCESS;
     if (o->path < HSMA_PATH_AUTO || o->path > HSMA_PATH_BLOCKED) return HSMA_STATUS_INVALID_VALUE;
+    if (o->inv < HSMA_INV_AUTO || o->inv > HSMA_INV_COLUMN) return HSMA_STATUS_INVALID_VALUE;
     if (o->path == HSMA_PATH_SMALL && m > 64) return HSMA_STATUS_INVALID_VALUE;
     if (o->nb != 0 && (!valid_nb(o->nb) || !nb_fits(o->nb, m, dtype)))
         return HSMA_STATUS_INVALID_VALUE;
@@ -247,13 +251,15 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
         return hip_status(medium_batched<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
 
     // Blocked path.
-    int nb = (opts && opts->nb) ? opts->nb : choose_nb(dt, m);
+    int nb = (opts && opts->nb) ? opts->nb : choose_nb(dt, m, n);
     if (!(opts && opts->nb)) {
         const int64_t cap = ((m + 15) / 16) * 16;
         if (nb > cap) nb = (int)cap;
     }
     int ib = (opts && opts->ib) ? opts->ib : (nb / 8 > 0 ? nb / 8 : 1);
     if (nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
+    const int route = opts ? opts->inv : HSMA_INV_AUTO;
+    if (!invert_route_applies<T>(m, nb, ib, route)) return HSMA_STATUS_INVALID_VALUE;
 
     // Phase events (single problems only: the *_ex entry points).
     PhaseRec rec;
@@ -281,8 +287,176 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     }
     for (int64_t b = 0; b < batch && e == hipSuccess; ++b)
         e = blocked_solve<T>(m, n, nb, ib, A + b * strideA, lda, B + b * strideB, ldb, (T *)work, s,
-                             timed ? &rec : nullptr);
+                             timed ? &rec : nullptr, route);
     if (timed) *opts->events_used = rec.used;
+    const hipError_t ef = workspace_free(work, s);
+    if (e != hipSuccess || ef != hipSuccess) return HSMA_STATUS_HIP_ERROR;
+    return HSMA_STATUS_SUCCESS;
+}
+
+// ---------------------------------------------------------------------------
+// Other TRSM variants (side, triangle, op, unit diagonal) through the
+// canonical left-side lower-triangular solve.
+//
+// With C = op(A) for the left side and C = op(A)^T for the right side
+// (X op(A) = alpha B <=> op(A)^T X^T = alpha B^T), every variant solves
+// C Y = alpha Bhat with Bhat = B (left) or B^T (right). C is lower
+// triangular as it stands, or after reversing the order of its rows and
+// columns (then Bhat's rows are reversed too). Both become strided views:
+// Ahat(i, j) = conj?(A[aoff + i*sai + j*saj]) lower triangular of order M,
+// Bhat(i, c) = B[boff + i*sbi + c*sbj], M x N.
+
+struct VariantView {
+    int64_t M, N;
+    int64_t aoff, sai, saj;
+    int64_t boff, sbi, sbj;
+    bool conj, unit;
+};
+
+VariantView variant_view(int side, int uplo, int trans, int diag, int64_t m, int64_t n,
+                         int64_t lda, int64_t ldb)
+{
+    VariantView v;
+    const bool left = side == HSMA_SIDE_LEFT;
+    const int64_t k = left ? m : n;
+    v.M = k;
+    v.N = left ? n : m;
+    v.conj = trans == HSMA_OP_C;
+    v.unit = diag == HSMA_DIAG_UNIT;
+    // C(i, j) is A(j, i) (conjugated for op C) when C "stores transposed"
+    const bool st = left ? trans != HSMA_OP_N : trans == HSMA_OP_N;
+    const bool op_lower = (uplo == HSMA_FILL_LOWER) == (trans == HSMA_OP_N);
+    const bool c_lower = left ? op_lower : !op_lower;
+    int64_t si = st ? lda : 1, sj = st ? 1 : lda;
+    v.aoff = 0;
+    if (!c_lower) {   // reverse the index order: Ahat(i, j) = C(k-1-i, k-1-j)
+        v.aoff = (k - 1) * (1 + lda);
+        si = -si;
+        sj = -sj;
+    }
+    v.sai = si;
+    v.saj = sj;
+    v.sbi = left ? 1 : ldb;
+    v.sbj = left ? ldb : 1;
+    v.boff = 0;
+    if (!c_lower) {
+        v.boff = (k - 1) * v.sbi;
+        v.sbi = -v.sbi;
+    }
+    return v;
+}
+
+template <typename T>
+hsma_status trsm_variant_impl(int side, int uplo, int trans, int diag, int64_t m, int64_t n,
+                              T alpha, const T *A, int64_t lda, int64_t strideA, T *B,
+                              int64_t ldb, int64_t strideB, int64_t batch, void *stream)
+{
+    constexpr int dt = traits<T>::dtype;
+    if (side < 0 || side > 1 || uplo < 0 || uplo > 1 || trans < 0 || trans > 2 || diag < 0 ||
+        diag > 1)
+        return HSMA_STATUS_INVALID_VALUE;
+    if (!traits<T>::is_complex && trans == HSMA_OP_C) trans = HSMA_OP_T;  // conj(a) = a
+    const int64_t k = side == HSMA_SIDE_LEFT ? m : n;
+    if (m < 0 || n < 0 || batch < 0) return HSMA_STATUS_INVALID_SIZE;
+    if (lda < imax(1, k) || ldb < imax(1, m)) return HSMA_STATUS_INVALID_SIZE;
+    if (strideA < 0 || strideB < 0) return HSMA_STATUS_INVALID_SIZE;
+    if (batch > 1 && strideB < ldb * n) return HSMA_STATUS_INVALID_SIZE;
+    if (side == HSMA_SIDE_LEFT && uplo == HSMA_FILL_LOWER && trans == HSMA_OP_N &&
+        diag == HSMA_DIAG_NON_UNIT)
+        return trsm_impl<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, nullptr, stream);
+    if (m == 0 || n == 0 || batch == 0) return HSMA_STATUS_SUCCESS;
+    if (!B) return HSMA_STATUS_INVALID_POINTER;
+    hipStream_t s = (hipStream_t)stream;
+    if (is_zero(alpha)) return hip_status(scale_matrix<T>(B, m, n, ldb, strideB, batch, alpha, true, s));
+    if (!A) return HSMA_STATUS_INVALID_POINTER;
+
+    const VariantView v = variant_view(side, uplo, trans, diag, m, n, lda, ldb);
+    const T *Ah = A + v.aoff;
+    T *Bh = B + v.boff;
+    const int64_t M = v.M, N = v.N;
+    if (M <= 64) {
+        // The lane-per-row kernel reads the views directly. A conjugated
+        // system conj(C) Y = alpha Bhat is solved as C conj(Y) =
+        // conj(alpha) conj(Bhat): Bhat is conjugated in place before and
+        // after the solve.
+        T a = alpha;
+        hipError_t e = hipSuccess;
+        if constexpr (traits<T>::is_complex) {
+            if (v.conj) {
+                a.im = -a.im;
+                e = tile_copy<T>(Bh, v.sbi, v.sbj, strideB, Bh, v.sbi, v.sbj, strideB, M, N, batch,
+                                 false, true, false, nullptr, s);
+            }
+        }
+        if (e == hipSuccess)
+            e = small_rowlane<T>(Ah, v.sai, v.saj, strideA, 0, Bh, v.sbi, v.sbj, strideB, 0, Bh, v.sbi,
+                                 v.sbj, strideB, 0, M, N, batch, 1, a, s, v.unit);
+        if constexpr (traits<T>::is_complex) {
+            if (v.conj && e == hipSuccess)
+                e = tile_copy<T>(Bh, v.sbi, v.sbj, strideB, Bh, v.sbi, v.sbj, strideB, M, N, batch,
+                                 false, true, false, nullptr, s);
+        }
+        return hip_status(e);
+    }
+
+    T one = zero_of(T());
+    if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
+    hipError_t e = hipSuccess;
+    void *work = nullptr;
+    if (batch > 1 && M <= kMediumMaxM) {
+        // gather every problem's Ahat triangle and alpha*Bhat, block rows of
+        // 64 over the whole batch, scatter X back
+        const size_t elems = (size_t)batch * (size_t)(M * M + M * N);
+        if (workspace_alloc(&work, elems * sizeof(T), s) != hipSuccess || !work) {
+            (void)hipGetLastError();
+            return HSMA_STATUS_ALLOC_FAILED;
+        }
+        T *Aw = (T *)work, *Bw = Aw + batch * M * M;
+        e = tile_copy<T>(Ah, v.sai, v.saj, strideA, Aw, 1, M, M * M, M, M, batch, true, v.conj,
+                         v.unit, nullptr, s);
+        if (e == hipSuccess)
+            e = tile_copy<T>(Bh, v.sbi, v.sbj, strideB, Bw, 1, M, M * N, M, N, batch, false, false,
+                             false, is_one(alpha) ? nullptr : &alpha, s);
+        if (e == hipSuccess) e = medium_batched<T>(M, N, one, Aw, M, M * M, Bw, M, M * N, batch, s);
+        if (e == hipSuccess)
+            e = tile_copy<T>(Bw, 1, M, M * N, Bh, v.sbi, v.sbj, strideB, M, N, batch, false, false,
+                             false, nullptr, s);
+    } else {
+        // one problem at a time: the triangle of Ahat into an M x M
+        // column-major copy, Bhat into an M x N one unless it is B itself
+        // (left side, no reversal), then the canonical blocked solve
+        const bool b_direct = v.sbi == 1 && v.boff == 0;
+        const int nb = choose_nb(dt, M, N);
+        const int64_t wblk = blocked_workspace_elems(M, N, nb);
+        const size_t elems = (size_t)(M * M + (b_direct ? 0 : M * N) + wblk);
+        if (workspace_alloc(&work, elems * sizeof(T), s) != hipSuccess || !work) {
+            (void)hipGetLastError();
+            return HSMA_STATUS_ALLOC_FAILED;
+        }
+        T *Aw = (T *)work;
+        T *Bw = b_direct ? nullptr : Aw + M * M;
+        T *Wk = Aw + M * M + (b_direct ? 0 : M * N);
+        for (int64_t b = 0; b < batch && e == hipSuccess; ++b) {
+            const T *Ab = Ah + b * strideA;
+            T *Bb = Bh + b * strideB;
+            e = tile_copy<T>(Ab, v.sai, v.saj, 0, Aw, 1, M, 0, M, M, 1, true, v.conj, v.unit,
+                             nullptr, s);
+            if (e != hipSuccess) break;
+            if (b_direct) {
+                if (!is_one(alpha)) e = scale_matrix<T>(Bb, M, N, ldb, 0, 1, alpha, false, s);
+                if (e == hipSuccess)
+                    e = blocked_solve<T>(M, N, nb, nb / 8 > 0 ? nb / 8 : 1, Aw, M, Bb, ldb, Wk, s);
+            } else {
+                e = tile_copy<T>(Bb, v.sbi, v.sbj, 0, Bw, 1, M, 0, M, N, 1, false, false, false,
+                                 is_one(alpha) ? nullptr : &alpha, s);
+                if (e == hipSuccess)
+                    e = blocked_solve<T>(M, N, nb, nb / 8 > 0 ? nb / 8 : 1, Aw, M, Bw, M, Wk, s);
+                if (e == hipSuccess)
+                    e = tile_copy<T>(Bw, 1, M, 0, Bb, v.sbi, v.sbj, 0, M, N, 1, false, false, false,
+                                     nullptr, s);
+            }
+        }
+    }
     const hipError_t ef = workspace_free(work, s);
     if (e != hipSuccess || ef != hipSuccess) return HSMA_STATUS_HIP_ERROR;
     return HSMA_STATUS_SUCCESS;
@@ -290,17 +464,27 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
 
 template <typename T>
 hsma_status diag_inv_impl(int64_t m, int32_t nb, int32_t ib, const T *A, int64_t lda, T *invA,
-                          void *stream)
+                          void *stream, int route = HSMA_INV_AUTO)
 {
     constexpr int dt = traits<T>::dtype;
     if (m < 0 || lda < imax(1, m)) return HSMA_STATUS_INVALID_SIZE;
-    if (nb == 0) nb = choose_nb(dt, m > 64 ? m : 65);
+    if (nb == 0) nb = choose_nb(dt, m > 64 ? m : 65, m > 64 ? m : 65);
     if (!valid_nb(nb) || !nb_fits(nb, m, dt)) return HSMA_STATUS_INVALID_VALUE;
     if (ib == 0) ib = nb / 8;
     if (ib < 1 || nb % ib != 0 || nb / ib > 64) return HSMA_STATUS_INVALID_VALUE;
+    if (route < HSMA_INV_AUTO || route > HSMA_INV_COLUMN) return HSMA_STATUS_INVALID_VALUE;
     if (m == 0) return HSMA_STATUS_SUCCESS;
+    if (!invert_route_applies<T>(m, nb, ib, route)) return HSMA_STATUS_INVALID_VALUE;
     if (!A || !invA) return HSMA_STATUS_INVALID_POINTER;
-    return hip_status(diag_invert_any<T>(m, nb, ib, A, lda, invA, (hipStream_t)stream));
+    return hip_status(diag_invert_any<T>(m, nb, ib, A, lda, invA, (hipStream_t)stream, route));
+}
+
+template <typename T>
+hsma_status diag_inv_ex_impl(int64_t m, const hsma_trsm_opts *o, const T *A, int64_t lda, T *invA,
+                             void *stream)
+{
+    return diag_inv_impl<T>(m, o ? o->nb : 0, o ? o->ib : 0, A, lda, invA, stream,
+                            o ? o->inv : HSMA_INV_AUTO);
 }
 
 template <typename T>
@@ -458,6 +642,29 @@ hsma_status hsma_diag_inv_z(int64_t m, int32_t nb, int32_t ib, const hsma_double
     HSMA_NOEXCEPT(diag_inv_impl<c64>(m, nb, ib, (const c64 *)A, lda, (c64 *)invA, stream))
 }
 
+hsma_status hsma_diag_inv_ex_s(int64_t m, const hsma_trsm_opts *opts, const float *A, int64_t lda,
+                               float *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_ex_impl<float>(m, opts, A, lda, invA, stream))
+}
+hsma_status hsma_diag_inv_ex_d(int64_t m, const hsma_trsm_opts *opts, const double *A,
+                               int64_t lda, double *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_ex_impl<double>(m, opts, A, lda, invA, stream))
+}
+hsma_status hsma_diag_inv_ex_c(int64_t m, const hsma_trsm_opts *opts,
+                               const hsma_float_complex *A, int64_t lda,
+                               hsma_float_complex *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_ex_impl<c32>(m, opts, (const c32 *)A, lda, (c32 *)invA, stream))
+}
+hsma_status hsma_diag_inv_ex_z(int64_t m, const hsma_trsm_opts *opts,
+                               const hsma_double_complex *A, int64_t lda,
+                               hsma_double_complex *invA, void *stream)
+{
+    HSMA_NOEXCEPT(diag_inv_ex_impl<c64>(m, opts, (const c64 *)A, lda, (c64 *)invA, stream))
+}
+
 hsma_status hsma_gemm_s(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                         const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                         int32_t a_lower, void *stream)
@@ -486,11 +693,85 @@ hsma_status hsma_gemm_z(int64_t M, int64_t N, int64_t K, double alpha,
                                  (c64 *)C, ldc, a_lower, stream))
 }
 
-int32_t hsma_trsm_block_size(int32_t dtype, int64_t m)
+hsma_status hsma_trsm_general_s(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, float alpha, const float *A, int64_t lda,
+                                float *B, int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<float>(side, uplo, trans, diag, m, n, alpha, A, lda, 0, B, ldb,
+                                           0, 1, stream))
+}
+hsma_status hsma_trsm_general_d(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, double alpha, const double *A, int64_t lda,
+                                double *B, int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<double>(side, uplo, trans, diag, m, n, alpha, A, lda, 0, B, ldb,
+                                            0, 1, stream))
+}
+hsma_status hsma_trsm_general_c(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, hsma_float_complex alpha,
+                                const hsma_float_complex *A, int64_t lda, hsma_float_complex *B,
+                                int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<c32>(side, uplo, trans, diag, m, n, from_abi(alpha),
+                                         (const c32 *)A, lda, 0, (c32 *)B, ldb, 0, 1, stream))
+}
+hsma_status hsma_trsm_general_z(int32_t side, int32_t uplo, int32_t trans, int32_t diag,
+                                int64_t m, int64_t n, hsma_double_complex alpha,
+                                const hsma_double_complex *A, int64_t lda, hsma_double_complex *B,
+                                int64_t ldb, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<c64>(side, uplo, trans, diag, m, n, from_abi(alpha),
+                                         (const c64 *)A, lda, 0, (c64 *)B, ldb, 0, 1, stream))
+}
+
+hsma_status hsma_trsm_strided_batched_general_s(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n, float alpha,
+                                                const float *A, int64_t lda, int64_t strideA,
+                                                float *B, int64_t ldb, int64_t strideB,
+                                                int64_t batch_count, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<float>(side, uplo, trans, diag, m, n, alpha, A, lda, strideA, B,
+                                           ldb, strideB, batch_count, stream))
+}
+hsma_status hsma_trsm_strided_batched_general_d(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n, double alpha,
+                                                const double *A, int64_t lda, int64_t strideA,
+                                                double *B, int64_t ldb, int64_t strideB,
+                                                int64_t batch_count, void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<double>(side, uplo, trans, diag, m, n, alpha, A, lda, strideA,
+                                            B, ldb, strideB, batch_count, stream))
+}
+hsma_status hsma_trsm_strided_batched_general_c(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n,
+                                                hsma_float_complex alpha,
+                                                const hsma_float_complex *A, int64_t lda,
+                                                int64_t strideA, hsma_float_complex *B,
+                                                int64_t ldb, int64_t strideB, int64_t batch_count,
+                                                void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<c32>(side, uplo, trans, diag, m, n, from_abi(alpha),
+                                         (const c32 *)A, lda, strideA, (c32 *)B, ldb, strideB,
+                                         batch_count, stream))
+}
+hsma_status hsma_trsm_strided_batched_general_z(int32_t side, int32_t uplo, int32_t trans,
+                                                int32_t diag, int64_t m, int64_t n,
+                                                hsma_double_complex alpha,
+                                                const hsma_double_complex *A, int64_t lda,
+                                                int64_t strideA, hsma_double_complex *B,
+                                                int64_t ldb, int64_t strideB, int64_t batch_count,
+                                                void *stream)
+{
+    HSMA_NOEXCEPT(trsm_variant_impl<c64>(side, uplo, trans, diag, m, n, from_abi(alpha),
+                                         (const c64 *)A, lda, strideA, (c64 *)B, ldb, strideB,
+                                         batch_count, stream))
+}
+
+int32_t hsma_trsm_block_size(int32_t dtype, int64_t m, int64_t n)
 {
     if (dtype < 0 || dtype > 3) return -1;
     if (m <= 64) return 0;
-    return choose_nb(dtype, m);
+    return choose_nb(dtype, m, n > 0 ? n : 1);
 }
 
 const char *hsma_status_string(hsma_status status)

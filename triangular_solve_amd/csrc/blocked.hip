@@ -21,7 +21,7 @@
 //    [[re, -im], [im, re]], so one complex multiply-add costs exactly the four
 //    real ones the flop count assumes.
 //  * copy_kernel - places the solved block row W into B.
-#include "../../include/hsma_trsm.h"
+#include "hsma_trsm.h"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -161,17 +161,22 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
                                   hipStream_t s);
 template <typename T>
 static bool blocked_inverse_applies(int64_t m, int nb);
+template <typename T>
+bool invert_route_applies(int64_t m, int nb, int ib, int route);
 // Inversion of all diagonal blocks: the blocked-inverse formula where it
 // applies (temporaries allocated stream-ordered), else diag_inv_kernel.
 template <typename T>
 hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
-                           hipStream_t s)
+                           hipStream_t s, int route)
 {
-    if (!blocked_inverse_applies<T>(m, nb)) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
+    if (!invert_route_applies<T>(m, nb, ib, route)) return hipErrorInvalidValue;
+    const bool merges = route == HSMA_INV_FUSED || route == HSMA_INV_BLOCKED ||
+                        (route == HSMA_INV_AUTO && blocked_inverse_applies<T>(m, nb));
+    if (!merges) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
     void *tmp = nullptr;
     hipError_t e = workspace_alloc(&tmp, (size_t)blocked_inverse_temp_elems(m, nb) * sizeof(T), s);
     if (e != hipSuccess) return e;
-    e = blocked_inverse<T>(m, nb, A, lda, invA, (T *)tmp, s);
+    e = blocked_invert<T>(m, nb, ib, A, lda, invA, (T *)tmp, s, route);
     const hipError_t ef = workspace_free(tmp, s);
     return e != hipSuccess ? e : ef;
 }
@@ -696,6 +701,185 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
 }
 
 // ---------------------------------------------------------------------------
+// Fused inversion of 2*I_B x 2*I_B diagonal blocks (the "traditional" fused
+// kernel of the HSMA-TRSM paper's blocked section, kept as an A/B route):
+// one workgroup holds a whole 2I_B x 2I_B diagonal block in LDS -- the
+// paper's 4 I_B^2 elements, which caps I_B at 64 (32 for double complex) on
+// gfx950's 160 KB -- inverts its two I_B x I_B diagonal blocks by
+// substitution against identity columns (one lane per column), then forms
+// the off-diagonal block of the inverse, -L22^{-1} L21 L11^{-1}, with two
+// small products in LDS (T = L21 L11^{-1} kept in the otherwise unused upper
+// right quarter). Larger blocks are then merged by the batched products of
+// blocked_inverse.
+
+template <typename T, int IB>
+__global__ void __launch_bounds__(256) fused_inv_kernel(const T *__restrict__ A, int64_t lda,
+                                                         int nb, T *__restrict__ invA)
+{
+    constexpr int S2 = 2 * IB;       // block order
+    constexpr int LD = S2 + 1;       // LDS column stride (element (i, j) at j*LD + i)
+    constexpr int RT = IB / 16;      // rows and columns of a thread's product sub-tile
+    static_assert(IB % 16 == 0, "I_B must be a multiple of 16");
+    extern __shared__ __attribute__((aligned(16))) char fused_lds[];
+    T *S = (T *)fused_lds;
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * S2;           // first row of this block in A
+    const T *D = A + r0 + r0 * lda;
+    T one = zero_of(T());
+    if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
+
+    // (0) the lower triangle of the block into LDS (the diagonal blocks'
+    // strictly upper parts are never read, the upper right quarter is T)
+    for (int e = tid; e < S2 * S2; e += 256) {
+        const int i = e % S2, j = e / S2;
+        if (j <= i) S[j * LD + i] = D[i + (int64_t)j * lda];
+    }
+    __syncthreads();
+
+    // (1) L11^{-1} and L22^{-1}: thread (q, c) solves L_qq y = e_c
+    if (tid < S2) {
+        const int q = tid / IB, c = tid % IB, o = q * IB;
+        T y[IB];
+#pragma unroll
+        for (int i = 0; i < IB; ++i) y[i] = i == c ? one : zero_of(T());
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const T r = recip(S[(o + j) * LD + o + j]);
+            y[j] = j >= c ? mul(y[j], r) : zero_of(T());   // exact zeros above the diagonal
+#pragma unroll
+            for (int i = j + 1; i < IB; ++i) y[i] = fms(y[i], S[(o + j) * LD + o + i], y[j]);
+        }
+        // every lane has read its block's coefficients before any overwrites them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+        for (int i = 0; i < IB; ++i) S[(o + c) * LD + o + i] = y[i];
+    }
+    __syncthreads();
+
+    // (2) -T = -L21 L11^{-1} into the upper right quarter: thread sub-tile
+    // of RT x RT outputs, rows ti*RT.., columns tj*RT..
+    const int ti = tid % 16, tj = tid / 16;
+    {
+        T acc[RT][RT];
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) acc[a][b] = zero_of(T());
+        for (int k = 0; k < IB; ++k) {
+            T l[RT], v[RT];
+#pragma unroll
+            for (int a = 0; a < RT; ++a) l[a] = S[k * LD + IB + ti * RT + a];          // L21(i, k)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) v[b] = S[(tj * RT + b) * LD + k];             // L11^{-1}(k, c)
+#pragma unroll
+            for (int a = 0; a < RT; ++a)
+#pragma unroll
+                for (int b = 0; b < RT; ++b) acc[a][b] = fms(acc[a][b], l[a], v[b]);    // -sum
+        }
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) S[(IB + tj * RT + b) * LD + ti * RT + a] = acc[a][b];
+    }
+    __syncthreads();
+
+    // (3) the inverse's lower left block, L22^{-1} (-T), over L21
+    {
+        T acc[RT][RT];
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) acc[a][b] = zero_of(T());
+        for (int k = 0; k < IB; ++k) {
+            T l[RT], v[RT];
+#pragma unroll
+            for (int a = 0; a < RT; ++a) l[a] = S[(IB + k) * LD + IB + ti * RT + a];   // L22^{-1}(i, k)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) v[b] = S[(IB + tj * RT + b) * LD + k];        // -T(k, c)
+#pragma unroll
+            for (int a = 0; a < RT; ++a)
+#pragma unroll
+                for (int b = 0; b < RT; ++b) acc[a][b] = fms(acc[a][b], l[a], v[b]);
+        }
+        __syncthreads();   // every thread's reads done before L21 is overwritten
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int b = 0; b < RT; ++b) {
+                // acc = -(L22^{-1} (-T)): stored negated
+                S[(tj * RT + b) * LD + IB + ti * RT + a] = fms(zero_of(T()), one, acc[a][b]);
+            }
+    }
+    __syncthreads();
+
+    // (4) the 2I_B x 2I_B inverse into invA (column-major, ld nb), zeros above
+    // the diagonal
+    const int64_t t = r0 / nb, off = r0 % nb;
+    T *out = invA + t * (int64_t)nb * nb + off + off * nb;
+    for (int e = tid; e < S2 * S2; e += 256) {
+        const int i = e % S2, j = e / S2;
+        out[i + (int64_t)j * nb] = (j <= i && !(i < IB && j >= IB)) ? S[j * LD + i] : zero_of(T());
+    }
+}
+
+// Largest fused inner block for the element type (4 I_B^2 elements in LDS).
+template <typename T>
+constexpr int fused_max_ib() { return sizeof(T) == 16 ? 32 : 64; }
+
+template <typename T>
+static bool fused_inverse_applies(int64_t m, int nb, int ib)
+{
+    return (ib == 32 || ib == 64) && ib <= fused_max_ib<T>() && m % nb == 0 && nb % (2 * ib) == 0;
+}
+
+template <typename T>
+static hipError_t fused_inverse(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
+                                T *temp, hipStream_t s)
+{
+    using R = typename traits<T>::real;
+    const int64_t nt = m / nb;
+    const int64_t total = nt * (int64_t)nb * nb;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(identity_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, invA, total,
+                       (int64_t)nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nblk = m / (2 * ib);
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)(2 * ib) * (2 * ib + 1) * sizeof(T);
+    if (ib == 64) {
+        if constexpr (fused_max_ib<T>() >= 64) {
+            hipLaunchKernelGGL((fused_inv_kernel<T, 64>), dim3((unsigned)nblk), dim3(256), lds, s, A,
+                               lda, nb, invA);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+        hipLaunchKernelGGL((fused_inv_kernel<T, 32>), dim3((unsigned)nblk), dim3(256), lds, s, A,
+                           lda, nb, invA);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // merge pairs of s x s inverses from 2 I_B up to N_B, as in blocked_inverse
+    for (int64_t sz = 2 * ib; sz < nb; sz *= 2) {
+        const int64_t pairs = nb / (2 * sz), batch = nt * pairs;
+        e = gemm_batched<T>(sz, sz, sz, R(1), A + sz, lda, 2 * sz * (lda + 1), (int64_t)nb * (lda + 1),
+                            invA, nb, 2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, R(0), temp, sz,
+                            sz * sz, pairs * sz * sz, pairs, batch, false, s);
+        if (e != hipSuccess) return e;
+        e = gemm_batched<T>(sz, sz, sz, R(-1), invA + sz * ((int64_t)nb + 1), nb,
+                            2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, temp, sz, sz * sz,
+                            pairs * sz * sz, R(0), invA + sz, nb, 2 * sz * ((int64_t)nb + 1),
+                            (int64_t)nb * nb, pairs, batch, false, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // Blocked driver
 
 template <typename T>
@@ -718,9 +902,24 @@ int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
 }
 
 template <typename T>
-hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
-                          hipStream_t s)
+bool invert_route_applies(int64_t m, int nb, int ib, int route)
 {
+    switch (route) {
+    case HSMA_INV_AUTO: return true;
+    case HSMA_INV_BLOCKED: return blocked_inverse_applies<T>(m, nb);
+    case HSMA_INV_FUSED: return fused_inverse_applies<T>(m, nb, ib);
+    case HSMA_INV_COLUMN: return nb <= 1024;
+    default: return false;
+    }
+}
+
+template <typename T>
+hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
+                          hipStream_t s, int route)
+{
+    if (!invert_route_applies<T>(m, nb, ib, route)) return hipErrorInvalidValue;
+    if (route == HSMA_INV_FUSED) return fused_inverse<T>(m, nb, ib, A, lda, invA, temp, s);
+    if (route == HSMA_INV_COLUMN) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
     return blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, temp, s)
                                              : diag_invert<T>(m, nb, ib, A, lda, invA, s);
 }
@@ -763,20 +962,22 @@ hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, 
 
 template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
-                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec)
+                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec, int route)
 {
     const int64_t nt = (m + nb - 1) / nb;
     T *invA = work;
     T *W = work + nt * nb * nb;   // also the inversion's temporary, before W is used
     hipError_t e = rec ? rec->mark(HSMA_PHASE_DIAG_INV, s) : hipSuccess;
-    if (e == hipSuccess) e = blocked_invert<T>(m, nb, ib, A, lda, invA, W, s);
+    if (e == hipSuccess) e = blocked_invert<T>(m, nb, ib, A, lda, invA, W, s, route);
     if (e == hipSuccess) e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec);
     return e;
 }
 
 #define HSMA_INST(T)                                                                              \
     template hipError_t diag_invert<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t);  \
-    template hipError_t diag_invert_any<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t); \
+    template hipError_t diag_invert_any<T>(int64_t, int, int, const T *, int64_t, T *, hipStream_t, \
+                                           int);                                                  \
+    template bool invert_route_applies<T>(int64_t, int, int, int);                                \
     template hipError_t gemm<T>(int64_t, int64_t, int64_t, typename traits<T>::real, const T *,    \
                                 int64_t, const T *, int64_t, typename traits<T>::real, T *,       \
                                 int64_t, bool, hipStream_t);                                      \
@@ -785,9 +986,9 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
                                         typename traits<T>::real, T *, int64_t, int64_t, int64_t, \
                                         hipStream_t);                                             \
     template hipError_t blocked_solve<T>(int64_t, int64_t, int, int, const T *, int64_t, T *,     \
-                                         int64_t, T *, hipStream_t, PhaseRec *);                  \
+                                         int64_t, T *, hipStream_t, PhaseRec *, int);             \
     template hipError_t blocked_invert<T>(int64_t, int, int, const T *, int64_t, T *, T *,        \
-                                          hipStream_t);                                           \
+                                          hipStream_t, int);                                      \
     template hipError_t blocked_apply<T>(int64_t, int64_t, int, const T *, int64_t, const T *, T *, \
                                          int64_t, T *, hipStream_t, PhaseRec *);
 HSMA_INST(float)

@@ -4,16 +4,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hsma_trsm.h"
 #include "common.hpp"
 
 namespace hsma {
 
-// Small regime, lane = row (any m <= 64, any strides; X may alias B).
+// Small regime, lane = row (any m <= 64, any strides, negative ones
+// included; X may alias B). unit: unit diagonal, the stored diagonal is not
+// read.
 template <typename T>
 hipError_t small_rowlane(const T *A, int64_t sai, int64_t saj, int64_t sa2, int64_t sa3,
                          const T *B, int64_t sbi, int64_t sbj, int64_t sb2, int64_t sb3,
                          T *X, int64_t sxi, int64_t sxj, int64_t sx2, int64_t sx3,
-                         int64_t m, int64_t n, int64_t ne02, int64_t ne03, T alpha, hipStream_t s);
+                         int64_t m, int64_t n, int64_t ne02, int64_t ne03, T alpha, hipStream_t s,
+                         bool unit = false);
 
 // Small regime, lane = right-hand-side column (m == 64, column-major, in place).
 template <typename T>
@@ -50,11 +54,15 @@ template <typename T>
 hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
                        hipStream_t s);
 
-// Same, choosing the blocked-inverse formula (small solver + batched GEMMs)
-// when m is a multiple of nb and nb of 64 (nb >= 128).
+// Same, by route (HSMA_INV_*): AUTO takes the blocked-inverse formula (small
+// solver + batched GEMMs) when m is a multiple of nb and nb of 64 (nb >= 128),
+// else the column substitution; FUSED inverts 2*ib blocks in LDS and merges.
+// A route that does not apply to (m, nb, ib) gives hipErrorInvalidValue.
 template <typename T>
 hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
-                           hipStream_t s);
+                           hipStream_t s, int route = 0);
+template <typename T>
+bool invert_route_applies(int64_t m, int nb, int ib, int route);
 
 // C = beta*C + alpha*A*B on the matrix cores (beta in {0, 1}); a_lower: A is
 // lower triangular (M == K) and its upper tiles are skipped.
@@ -96,7 +104,8 @@ inline int blocked_phase_events(int64_t nt) { return (int)(3 * nt + 1); }
 int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb);
 template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
-                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec = nullptr);
+                         int64_t ldb, T *work, hipStream_t s, PhaseRec *rec = nullptr,
+                         int route = 0);
 
 // The two halves of blocked_solve. blocked_invert: all diagonal blocks into
 // invA (ceil(m/nb) blocks of nb x nb), using temp (blocked_inverse_temp_elems
@@ -105,7 +114,7 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
 int64_t blocked_inverse_temp_elems(int64_t m, int nb);
 template <typename T>
 hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
-                          hipStream_t s);
+                          hipStream_t s, int route = 0);
 template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
                          T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec = nullptr);
@@ -127,8 +136,18 @@ hipError_t small_path(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
                             m, n, batch, 1, alpha, s);
 }
 
-// Outer block size for an m x m problem of the given dtype code: the table
-// by nearest size, or the HSMA_NB override (api.cpp).
-int choose_nb(int dtype, int64_t m);
+// dst(i, j) = f(src(i, j)) for i < rows, j < cols (only j <= i when lower)
+// of batch problems: element (i, j) of problem b at src[b*ssb + i*ssi +
+// j*ssj], dst alike (strides of either sign). f conjugates (conj), puts 1 on
+// the diagonal without reading it (unit) and multiplies by *alpha (when
+// alpha is not NULL).
+template <typename T>
+hipError_t tile_copy(const T *src, int64_t ssi, int64_t ssj, int64_t ssb, T *dst, int64_t dsi,
+                     int64_t dsj, int64_t dsb, int64_t rows, int64_t cols, int64_t batch,
+                     bool lower, bool conj, bool unit, const T *alpha, hipStream_t s);
+
+// Outer block size for an m x m system with n right-hand sides of the given
+// dtype code: the table by nearest shape, or the HSMA_NB override (api.cpp).
+int choose_nb(int dtype, int64_t m, int64_t n);
 
 }  // namespace hsma

@@ -20,7 +20,7 @@
 #include <cstdlib>
 #include <mutex>
 
-#include "../../include/hsma_trsm.h"
+#include "hsma_trsm.h"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -79,7 +79,7 @@ struct Plan {
 bool make_plan(int dtype, int64_t m, int64_t n, size_t elem, Plan *out)
 {
     const int64_t budget = (int64_t)(usable_bytes() / elem);
-    int nb = choose_nb(dtype, m);
+    int nb = choose_nb(dtype, m, n);
     while (true) {
         const int64_t nt = (m + nb - 1) / nb;
         const int64_t inv = nt * (int64_t)nb * nb;

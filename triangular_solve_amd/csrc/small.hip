@@ -49,7 +49,19 @@ struct RowlaneArgs {
     int64_t ne02;
     int64_t sa2, sa3, sb2, sb3, sx2, sx3;
     T alpha;
+    int unit;  // unit diagonal: a_ii = 1, the stored diagonal is not read
 };
+
+// One, as the first element of a float or double array, for the unit
+// diagonal: its address stands in for the diagonal with stride 0.
+__device__ const float kOneF[2] = {1.0f, 0.0f};
+__device__ const double kOneD[2] = {1.0, 0.0};
+template <typename T>
+__device__ __forceinline__ const T *unit_one()
+{
+    if constexpr (std::is_same<typename traits<T>::real, float>::value) return (const T *)kOneF;
+    else return (const T *)kOneD;
+}
 
 constexpr int kLdsStride = 65;  // padded LDS column stride of the staged triangle
 
@@ -74,8 +86,11 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
 
     T one = zero_of(T());
     if constexpr (traits<T>::is_complex) one.re = 1; else one = 1;
-    // Lane i owns row i: its own 1/a_ii, no exchange needed.
-    const T inv = recip(lane < m ? Ab[lane * (p.sai + p.saj)] : one);
+    // Lane i owns row i: its own 1/a_ii, no exchange needed. A unit
+    // diagonal reads the constant one instead (stride 0).
+    const T *dg = p.unit ? unit_one<T>() : Ab;
+    const int64_t sdg = p.unit ? 0 : p.sai + p.saj;
+    const T inv = recip(lane < m ? dg[lane * sdg] : one);
 
     if constexpr (RR) {
         static_assert(!traits<T>::is_complex, "row registers for real types only");
@@ -201,9 +216,11 @@ template <typename T>
 hipError_t small_rowlane(const T *A, int64_t sai, int64_t saj, int64_t sa2, int64_t sa3,
                          const T *B, int64_t sbi, int64_t sbj, int64_t sb2, int64_t sb3,
                          T *X, int64_t sxi, int64_t sxj, int64_t sx2, int64_t sx3,
-                         int64_t m, int64_t n, int64_t ne02, int64_t ne03, T alpha, hipStream_t s)
+                         int64_t m, int64_t n, int64_t ne02, int64_t ne03, T alpha, hipStream_t s,
+                         bool unit)
 {
     RowlaneArgs<T> p;
+    p.unit = unit ? 1 : 0;
     p.A = A; p.B = B; p.X = X;
     p.m = (int)m; p.n = (int)n;
     p.sai = sai; p.saj = saj; p.sbi = sbi; p.sbj = sbj; p.sxi = sxi; p.sxj = sxj;
@@ -877,7 +894,7 @@ hipError_t scale_matrix(T *B, int64_t m, int64_t n, int64_t ldb, int64_t strideB
     template hipError_t small_rowlane<T>(const T *, int64_t, int64_t, int64_t, int64_t, const T *, \
                                          int64_t, int64_t, int64_t, int64_t, T *, int64_t, int64_t, \
                                          int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, T,   \
-                                         hipStream_t);                                             \
+                                         hipStream_t, bool);                                       \
     template hipError_t small_colane<T>(int64_t, T, const T *, int64_t, int64_t, T *, int64_t,     \
                                         int64_t, int64_t, hipStream_t);                            \
     template hipError_t small_colane2<T>(int64_t, T, const T *, int64_t, int64_t, int64_t, T *,    \
