@@ -281,6 +281,137 @@ def bench_blocked(hs, torch, m, dtypes, runs=4, nb=0, cpu=True):
     return out
 
 
+VARIANTS = [(s, u, t, d) for s in "LR" for u in "LU" for t in "NTC" for d in "NU"]
+
+
+def bench_variants(hs, torch, m=8192, dtypes=("f32", "f64"), runs=2, nvec=8):
+    """Every TRSM variant (side, triangle, op, diagonal) at m = n, one solve
+    each after a warm-up: ms, LAPACK GFLOPS, MFMA fraction, and nvec sampled
+    right-hand-side vectors (columns for the left side, rows for the right
+    side) against the oracle's variant solve. For real types op C equals T
+    and is not repeated."""
+    import oracle
+    import synth
+    out = {}
+    stream = torch.cuda.current_stream()
+    for dt in dtypes:
+        log("variants", dt, m)
+        host = {"L": synth.tri(dt, m, seed=SEED_CFG3), "U": synth.tri(dt, m, seed=SEED_CFG3, layout="row")}
+        B = synth.rhs(dt, m, m, seed=SEED_CFG3 + 1)
+        dAs = {u: torch.from_numpy(a).cuda() for u, a in host.items()}
+        dB0 = torch.from_numpy(B).cuda()
+        dB = dB0.clone()
+        f = hs.entry("general", dt)
+        Bv = B[0].T                      # [i, c]
+        sel = synth.pick_columns(m, nvec, seed=SEED_CFG3 + 7)
+        for (side, uplo, trans, diag) in VARIANTS:
+            if trans == "C" and not dt.startswith("c"):
+                continue
+            if diag == "U":
+                continue     # same kernels as the non-unit case (the diagonal reads a constant)
+            codes = (hs.SIDE[side], hs.UPLO[uplo], hs.OP[trans], hs.DIAG[diag])
+            times = []
+            for r in range(runs + 1):
+                dB.copy_(dB0)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                st = f(*codes, m, m, 1.0, dAs[uplo], m, dB, m, stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                hs.check(st, "general_" + dt)
+                times.append(a.elapsed_time(b))
+            ms = float(np.mean(times[1:]))
+            Xg = dB[0].cpu().numpy().T           # [i, c]
+            Av = host[uplo][0].T
+            if side == "L":
+                Xo = oracle.trsm_general(Av, np.ascontiguousarray(Bv[:, sel]), side, uplo, trans, diag)
+                got = Xg[:, sel]
+            else:
+                Xo = oracle.trsm_general(Av, np.ascontiguousarray(Bv[sel, :]), side, uplo, trans, diag)
+                got = Xg[sel, :]
+            err = float(np.linalg.norm(got.astype(Xo.dtype) - Xo) / np.linalg.norm(Xo))
+            flops = lapack_flops(dt, m, m)
+            out["%s %s%s%s%s" % (dt, side, uplo, trans, diag)] = {
+                "ms": ms, "gflops": flops / ms / 1e6, "mfma_peak_frac": flops / ms / 1e9 / MFMA_PEAK_TFLOPS[dt],
+                "rel_err_%d" % nvec: err}
+        del dAs, dB0, dB, host, B
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_inversion(hs, torch, cases=((8192, 2048), (8192, 1024), (1024, 256), (1024, 128)),
+                    dtypes=DTYPES, runs=5):
+    """The diagonal-block inversion alone, per route (blocked-inverse formula
+    from 64 x 64 sub-blocks; fused 2*I_B blocks in LDS then merges; column
+    substitution), ms per call (mean of `runs` after a warm-up)."""
+    import synth
+    out = {}
+    stream = torch.cuda.current_stream()
+    tdt = {"f32": torch.float32, "f64": torch.float64, "c64": torch.complex64, "c128": torch.complex128}
+    for dt in dtypes:
+        for m in sorted({m for m, _ in cases}):
+            A = torch.from_numpy(synth.tri(dt, m, seed=SEED_CFG3)).cuda()
+            for (mm, nb) in cases:
+                if mm != m or (dt == "c128" and nb > 512 and m % nb):
+                    continue
+                inv = torch.empty(m // nb * nb * nb, dtype=tdt[dt], device="cuda")
+                routes = [("blocked", {"inv": hs.INV_BLOCKED})]
+                for ib in (64, 32):
+                    if not (ib == 64 and dt == "c128") and nb % (2 * ib) == 0:
+                        routes.append(("fused_ib%d" % ib, {"inv": hs.INV_FUSED, "ib": ib}))
+                if nb <= 1024:
+                    routes.append(("column", {"inv": hs.INV_COLUMN}))
+                res = {}
+                for name, o in routes:
+                    f = hs.entry("diag_inv_ex", dt)
+                    hs.check(f(m, dict(o, nb=nb), A, m, inv, stream), "diag_inv_ex " + name)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for _ in range(runs):
+                        f(m, dict(o, nb=nb), A, m, inv, stream)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    res[name] = a.elapsed_time(b) / runs
+                out["%s m=%d nb=%d" % (dt, m, nb)] = res
+                del inv
+            del A
+            torch.cuda.empty_cache()
+    return out
+
+
+def bench_few_rhs(hs, torch, m=8192, n=64, dtypes=DTYPES, runs=5):
+    """Few right-hand sides (m x m, n columns), N_B from the (m, n) table."""
+    import oracle
+    import synth
+    out = {}
+    stream = torch.cuda.current_stream()
+    for dt in dtypes:
+        A = synth.tri(dt, m, seed=SEED_CFG3)
+        B = synth.rhs(dt, m, n, seed=SEED_CFG3 + 1)
+        dA, dB0 = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dB = dB0.clone()
+        f = hs.entry("trsm", dt)
+        times = []
+        for r in range(runs + 1):
+            dB.copy_(dB0)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hs.check(f(m, n, 1.0, dA, m, dB, m, stream), "trsm_" + dt)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = float(np.mean(times[1:]))
+        Xg = dB[0].cpu().numpy().T[:, :8]
+        Xo = oracle.trsm(A[0].T, np.ascontiguousarray(B[0].T[:, :8]))
+        flops = lapack_flops(dt, m, n)
+        out[dt] = {"ms": ms, "gflops": flops / ms / 1e6, "nb": hs.hsma_trsm_block_size(hs.DTYPE_CODE[dt], m, n),
+                   "rel_err_8cols": float(np.linalg.norm(Xg.astype(Xo.dtype) - Xo) / np.linalg.norm(Xo))}
+        del dA, dB0, dB
+    return out
+
+
 def medium_workload(hs, torch, m=128, n=64, batch=1024, reps=5):
     """Strided batches in the 64 < m <= 256 band (block rows of 64 over the
     whole batch): ms per batched call and GFLOPS per dtype, plus 64-problem
@@ -413,7 +544,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched",
-                    choices=["batched", "blocked", "counters", "medium", "gemm"],
+                    choices=["batched", "blocked", "counters", "medium", "gemm", "variants", "inversion"],
                     help="counters: only three batched solves per dtype and a 1 GiB copy, for "
                          "rocprofv3 --pmc runs; medium: strided batches of 1024 systems with "
                          "m = 128, n = 64; gemm: the library GEMM at trailing-update shapes")
@@ -438,9 +569,10 @@ def main():
     if args.workload == "counters":
         counter_workload(hs, torch)
         return
-    if args.workload in ("medium", "gemm"):
-        res = medium_workload(hs, torch) if args.workload == "medium" else gemm_workload(hs, torch)
-        print(json.dumps({"workload": args.workload, "results": res}), flush=True)
+    if args.workload in ("medium", "gemm", "variants", "inversion"):
+        fn = {"medium": medium_workload, "gemm": gemm_workload, "variants": bench_variants,
+              "inversion": bench_inversion}[args.workload]
+        print(json.dumps({"workload": args.workload, "results": fn(hs, torch)}), flush=True)
         return
     if args.workload == "blocked":
         dts = args.dtypes.split(",")
@@ -470,10 +602,15 @@ def main():
     st = bench_solve_tri(hs, torch)
     log("solve_tri 128 shape")
     st128 = bench_solve_tri(hs, torch, runs=1000, n=128, k=8, e2=4, e3=1)
-    blocked = blocked16 = None
+    blocked = blocked16 = variants = inversion = few = None
     if not args.no_blocked:
         blocked = bench_blocked(hs, torch, 8192, DTYPES, runs=3)
         blocked16 = bench_blocked(hs, torch, 16384, ["f32", "f64", "c128"], runs=2)
+        log("few right-hand sides")
+        few = bench_few_rhs(hs, torch)
+        variants = bench_variants(hs, torch)
+        log("inversion routes")
+        inversion = bench_inversion(hs, torch)
     cpu = None if args.no_cpu else cpu_baseline(bt["host"])
     line = {
         "metric": METRIC, "value": bt["gflops"], "unit": "GFLOPS", "n_gpus": 1, "steps": args.steps,
@@ -490,6 +627,9 @@ def main():
         "solve_tri": st, "solve_tri_128": st128,
         "blocked_8192": blocked,
         "blocked_16384": blocked16,
+        "few_rhs_8192x64": few,
+        "variants_8192": variants,
+        "inversion_routes_ms": inversion,
     }
     print(json.dumps(line), flush=True)
 
