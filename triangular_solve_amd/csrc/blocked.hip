@@ -619,6 +619,80 @@ hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha,
 }
 
 // ---------------------------------------------------------------------------
+// Split-K for products with few output tiles (few right-hand sides): with
+// N <= 128 a product has one column of 128 x 128 tiles, so a trailing
+// update of M rows runs on M/128 workgroups for 256 CUs. The K range is cut
+// into S equal chunks; a batched product writes the S partial products
+// P_s = A[:, K_s] B[K_s, :] to workspace, and reduce_kernel forms
+// C = beta C + alpha (P_0 + ... + P_{S-1}), summing in a fixed order so the
+// result is the same on every run.
+
+template <typename R>
+__global__ void __launch_bounds__(256) reduce_kernel(const R *__restrict__ P, int64_t rows,
+                                                     int64_t cols, int64_t S, R alpha, R beta,
+                                                     R *__restrict__ C, int64_t ldc)
+{
+    const int64_t total = rows * cols;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        R acc = P[e];
+        for (int64_t k = 1; k < S; ++k) acc += P[k * total + e];
+        const int64_t i = e % rows, j = e / rows;
+        R *c = C + i + j * ldc;
+        *c = beta == R(0) ? alpha * acc : beta * *c + alpha * acc;
+    }
+}
+
+constexpr int kSplitTarget = 512;   // workgroups a split product aims for (2 per CU)
+constexpr int kSplitMinChunk = 256; // smallest K chunk
+
+// Chunks for an M x N x K product (elements of T), 1 = no split.
+template <typename T>
+int64_t splitk_chunks(int64_t M, int64_t N, int64_t K, int64_t part_elems)
+{
+    const int64_t f = traits<T>::is_complex ? 2 : 1;
+    const int64_t tiles = ((M * f + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    if (tiles >= 256 || K < 2 * kSplitMinChunk || M * N <= 0) return 1;
+    int64_t S = (kSplitTarget + tiles - 1) / tiles;
+    if (S > K / kSplitMinChunk) S = K / kSplitMinChunk;
+    if (S > part_elems / (M * N)) S = part_elems / (M * N);
+    while (S > 1 && K % S != 0) --S;
+    return S < 1 ? 1 : S;
+}
+
+int64_t splitk_part_elems(int64_t m, int64_t n)
+{
+    // partials of at most kSplitTarget tiles' worth of rows (plus one tile
+    // of rounding) for n <= 256; larger n has enough tiles
+    if (n > 256) return 0;
+    const int64_t rows = (int64_t)kSplitTarget * kBM + 16 * (int64_t)kBM;
+    return (rows < 16 * m ? rows : 16 * m) * n;
+}
+
+template <typename T>
+hipError_t gemm_splitk(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
+                       int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
+                       int64_t ldc, bool a_lower, T *part, int64_t part_elems, hipStream_t s)
+{
+    using R = typename traits<T>::real;
+    const int64_t S = part ? splitk_chunks<T>(M, N, K, part_elems) : 1;
+    if (S <= 1) return gemm<T>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower, s);
+    const int64_t Kc = K / S;
+    // partial s: A[:, s*Kc ..] B[s*Kc .., :] into part + s*M*N (ld M); a
+    // triangular A runs as a full one (its upper part holds exact zeros)
+    hipError_t e = gemm_batched<T>(M, N, Kc, R(1), A, lda, Kc * lda, 0, B, ldb, Kc, 0, R(0), part, M,
+                                   M * N, 0, S, S, false, s);
+    if (e != hipSuccess) return e;
+    constexpr int64_t f = traits<T>::is_complex ? 2 : 1;
+    const int64_t total = M * f * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(reduce_kernel<R>, dim3((unsigned)blocks), dim3(256), 0, s, (const R *)part,
+                       M * f, N, S, alpha, beta, (R *)C, ldc * f);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Diagonal-block inversion by the blocked-inverse formula
 //
 // The HSMA-TRSM paper's two-level blocking reuses the small-scale solver for
@@ -898,7 +972,8 @@ int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
     int64_t w = (int64_t)nb * n;
     const int64_t t = blocked_inverse_temp_elems(m, nb);
     if (t > w) w = t;  // the merge temporaries live in W before W is used
-    return nt * nb * nb + w;
+    w = (w + 63) / 64 * 64;   // the split-K partials start 256-byte aligned
+    return nt * nb * nb + w + splitk_part_elems(m, n);
 }
 
 template <typename T>
@@ -926,7 +1001,8 @@ hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T 
 
 template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
-                         T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec)
+                         T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec, T *part,
+                         int64_t part_elems)
 {
     using R = typename traits<T>::real;
     const int64_t nt = (m + nb - 1) / nb;
@@ -938,7 +1014,8 @@ hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, 
         // X_t = D_t^{-1} B_t (D_t^{-1} is lower triangular: upper tiles skipped)
         e = mark(HSMA_PHASE_INV_GEMM);
         if (e == hipSuccess)
-            e = gemm<T>(rb, n, rb, R(1), invA + t * nb * nb, nb, B + r0, ldb, R(0), W, nb, true, s);
+            e = gemm_splitk<T>(rb, n, rb, R(1), invA + t * nb * nb, nb, B + r0, ldb, R(0), W, nb, true,
+                               part, part_elems, s);
         if (e == hipSuccess) e = mark(HSMA_PHASE_COPY);
         if (e != hipSuccess) break;
         for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += 65535) {
@@ -952,8 +1029,8 @@ hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, 
         if (r0 + rb < m) {
             e = mark(HSMA_PHASE_TRAILING);
             if (e == hipSuccess)
-                e = gemm<T>(m - r0 - rb, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb, R(1),
-                            B + r0 + rb, ldb, false, s);
+                e = gemm_splitk<T>(m - r0 - rb, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb,
+                                   R(1), B + r0 + rb, ldb, false, part, part_elems, s);
         }
     }
     if (e == hipSuccess) e = mark(HSMA_PHASE_END);
@@ -967,9 +1044,17 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     const int64_t nt = (m + nb - 1) / nb;
     T *invA = work;
     T *W = work + nt * nb * nb;   // also the inversion's temporary, before W is used
+    int64_t wlen = (int64_t)nb * n;
+    const int64_t tl = blocked_inverse_temp_elems(m, nb);
+    if (tl > wlen) wlen = tl;
+    wlen = (wlen + 63) / 64 * 64;
+    T *part = W + wlen;           // split-K partial products (few right-hand sides)
+    const int64_t part_elems = splitk_part_elems(m, n);
     hipError_t e = rec ? rec->mark(HSMA_PHASE_DIAG_INV, s) : hipSuccess;
     if (e == hipSuccess) e = blocked_invert<T>(m, nb, ib, A, lda, invA, W, s, route);
-    if (e == hipSuccess) e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec);
+    if (e == hipSuccess)
+        e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec, part_elems ? part : nullptr,
+                             part_elems);
     return e;
 }
 
@@ -990,7 +1075,7 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     template hipError_t blocked_invert<T>(int64_t, int, int, const T *, int64_t, T *, T *,        \
                                           hipStream_t, int);                                      \
     template hipError_t blocked_apply<T>(int64_t, int64_t, int, const T *, int64_t, const T *, T *, \
-                                         int64_t, T *, hipStream_t, PhaseRec *);
+                                         int64_t, T *, hipStream_t, PhaseRec *, T *, int64_t);
 HSMA_INST(float)
 HSMA_INST(double)
 HSMA_INST(c32)

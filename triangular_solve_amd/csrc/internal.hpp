@@ -115,9 +115,12 @@ int64_t blocked_inverse_temp_elems(int64_t m, int nb);
 template <typename T>
 hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
                           hipStream_t s, int route = 0);
+// part (part_elems elements, may be NULL) holds split-K partial products
+// for products with few output tiles.
 template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
-                         T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec = nullptr);
+                         T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec = nullptr,
+                         T *part = nullptr, int64_t part_elems = 0);
 
 // Small-regime dispatch on column-major storage, in place (m <= 64): the
 // lane-per-column kernel needs the full 64 rows, enough columns to fill a
