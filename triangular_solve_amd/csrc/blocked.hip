@@ -270,14 +270,10 @@ struct GemmArgs {
     // of T) and B, C shifted likewise (real units).
     int64_t bin;
     int64_t sAi, sAo, sBi, sBo, sCi, sCo;
-    // Lower-triangular A: workgroup x computes row tiles x and (tiles-1-x),
-    // a light and a heavy one (K grows with the row), so all workgroups carry
-    // about the same number of K steps.
-    int pair;
 };
 
-template <typename T, bool VEC, bool PAIR>
-__global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 {
     using R = typename traits<T>::real;
     using cfg = mfma_cfg<R>;
@@ -303,9 +299,17 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
     // groups of kGroupRows row tiles, so the workgroups resident on one XCD
     // share a few A row panels and B column panels.
     int64_t bx = blockIdx.x, by = blockIdx.y;
-    if constexpr (!PAIR) {
+    {
         const int64_t gx = gridDim.x, gy = gridDim.y, total = gx * gy;
-        if (gridDim.z == 1 && total % kXcds == 0) {
+        if (p.a_lower) {
+            // Triangular A: row tile x carries x + 1 K blocks. The heaviest
+            // row tiles are dispatched first (consecutive ids, dealt to the
+            // XCDs in turn, take the column tiles of one row tile), so the
+            // light ones fill in at the end.
+            const int64_t id = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gx;
+            bx = gx - 1 - id / gy;
+            by = id % gy;
+        } else if (gridDim.z == 1 && total % kXcds == 0) {
             const int64_t id = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gx;
             const int64_t t = (id % kXcds) * (total / kXcds) + id / kXcds;
             const int64_t first = t / (kGroupRows * gy) * kGroupRows;
@@ -315,7 +319,7 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
             by = r / gs;
         }
     }
-    int64_t i0 = bx * kBM;  // row tile; reassigned per paired tile below
+    const int64_t i0 = bx * kBM;
     const int64_t j0 = by * kBN;
     {
         const int64_t z = blockIdx.z, g = z / p.bin, k = z % p.bin;
@@ -323,8 +327,6 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
         p.B += g * p.sBo + k * p.sBi;
         p.C += g * p.sCo + k * p.sCi;
     }
-
-    int64_t kend = p.Kr;
 
     // ---- staging of one K step: A as 16-byte chunks along i, B along k ----
     // A tile: BK x kBM reals = (kBM/VN) chunks per k row; chunks per thread:
@@ -339,7 +341,9 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
 
     // Interior tiles and steps (the common case) take branch-free 16-byte
     // loads; the bounds and triangle checks only run at the edges.
-    bool tile_interior = false;
+    int64_t kend = p.Kr;
+    if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
+    const bool tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;
     auto load_step = [&](int64_t k0, int slot) {
         const bool fast = tile_interior && k0 + BK <= p.Kr && (!p.a_lower || k0 + BK <= i0 + 1);
         {
@@ -452,14 +456,6 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
         else return lg + 4 * r;
     };
 
-    const int64_t ntile_rows = (p.Mr + kBM - 1) / kBM;
-    const int nrep = (PAIR && 2 * bx + 1 != ntile_rows) ? 2 : 1;
-    for (int rep = 0; rep < (PAIR ? 2 : 1); ++rep) {
-    if (rep >= nrep) break;
-    i0 = (rep == 0 ? bx : ntile_rows - 1 - bx) * kBM;
-    kend = p.Kr;
-    if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
-    tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;
     typename cfg::acc_t acc[NBK][NBK];
 #pragma unroll
     for (int b = 0; b < NBK; ++b)
@@ -531,7 +527,6 @@ __global__ void __launch_bounds__(256, PAIR ? 1 : 2) gemm_kernel(GemmArgs<T> p)
                     *cp = p.alpha * v;
                 }
             }
-    }  // paired row tiles
 }
 
 // Batched product: batch = nout * bin products; product z = g*bin + k uses
@@ -557,7 +552,6 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     p.N = N;
     p.Kr = K * f;
     p.a_lower = a_lower ? 1 : 0;
-    p.pair = a_lower ? 1 : 0;
     p.bin = bin > 0 ? bin : 1;
     p.sAi = sAi; p.sAo = sAo;
     p.sBi = sBi * f; p.sBo = sBo * f;
@@ -572,8 +566,7 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
         p.alpha = alpha;
         p.cscale = beta / alpha;
     }
-    int64_t gx = (p.Mr + kBM - 1) / kBM;
-    if (p.pair) gx = (gx + 1) / 2;
+    const int64_t gx = (p.Mr + kBM - 1) / kBM;
     const int64_t gy = (N + kBN - 1) / kBN;
     if (gx > 0x7fffffff || gy > 65535 || batch > 65535) return hipErrorInvalidConfiguration;
     // 16-byte loads need 16-byte aligned columns of A and B (every batch member).
@@ -582,13 +575,8 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
                      (ldb * sz) % 16 == 0 && (sAi * sz) % 16 == 0 && (sAo * sz) % 16 == 0 &&
                      (sBi * sz) % 16 == 0 && (sBo * sz) % 16 == 0;
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)batch);
-    if (p.pair) {
-        if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, true>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<T, false, true>), grid, dim3(256), 0, s, p);
-    } else {
-        if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, false>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<T, false, false>), grid, dim3(256), 0, s, p);
-    }
+    if (vec) hipLaunchKernelGGL((gemm_kernel<T, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_kernel<T, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -761,10 +749,9 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
                             sz * sz, pairs * sz * sz, pairs, batch, false, s);
         if (e != hipSuccess) return e;
         // inv21 = -inv22 * T. inv22 is lower triangular with exact zeros above
-        // its diagonal, so it is multiplied as a full matrix: the zero tiles
-        // add exact zeros, and the full product keeps all its tiles in
-        // flight (the triangular form pairs row tiles and halves the
-        // workgroups, which leaves CUs idle at these batch sizes).
+        // its diagonal; it is multiplied as a full matrix (the zero tiles add
+        // exact zeros): at these sizes skipping them measured no faster for
+        // f32 and f64.
         e = gemm_batched<T>(sz, sz, sz, R(-1), invA + sz * ((int64_t)nb + 1), nb,
                             2 * sz * ((int64_t)nb + 1), (int64_t)nb * nb, temp, sz, sz * sz,
                             pairs * sz * sz, R(0), invA + sz, nb, 2 * sz * ((int64_t)nb + 1),
