@@ -21,6 +21,8 @@
 //    [[re, -im], [im, re]], so one complex multiply-add costs exactly the four
 //    real ones the flop count assumes.
 //  * copy_kernel - places the solved block row W into B.
+#include <type_traits>
+
 #include "hsma_trsm.h"
 #include "common.hpp"
 #include "internal.hpp"
@@ -218,18 +220,35 @@ hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *in
 // sub-steps is one contiguous 16-byte LDS read (the same permutation is used
 // for A, so every k is still summed exactly once).
 
-template <typename R> struct mfma_cfg;
+// NI x NJ blocks of BLK x BLK outputs per wave (NI along the rows i of C, NJ
+// along its columns j), four waves as 2 x 2, so a workgroup tile is
+// BM = 2*NI*BLK rows by BN = 2*NJ*BLK columns; K steps of BK. WIDE selects
+// the tall f32 tile for large products.
+template <typename R, bool WIDE = false> struct mfma_cfg;
 // FP32: v_mfma_f32_32x32x2f32, a wave owns 64 x 64 outputs as 2 x 2 blocks.
-template <> struct mfma_cfg<float> {
-    static constexpr int BLK = 32, LG = 2, NB = 2, BK = 32;  // LG: lane groups along k
+template <> struct mfma_cfg<float, false> {
+    static constexpr int BLK = 32, LG = 2, NI = 2, NJ = 2, BK = 32;  // LG: lane groups along k
     using acc_t = f32x16;
     static constexpr int NACC = 16;
+    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
 };
-// FP64: v_mfma_f64_16x16x4f64, a wave owns 64 x 64 outputs as 4 x 4 blocks.
-template <> struct mfma_cfg<double> {
-    static constexpr int BLK = 16, LG = 4, NB = 4, BK = 16;
+// FP32, wide: a wave owns 128 x 64 outputs as 4 x 2 blocks, a 256 x 128
+// workgroup tile with K steps of 16: a third fewer LDS bytes per MFMA and
+// more flops per byte of L2 traffic. It wins on large products (the trailing
+// updates, K >= 2048) and loses where its coarser tiles leave CUs idle.
+template <> struct mfma_cfg<float, true> {
+    static constexpr int BLK = 32, LG = 2, NI = 4, NJ = 2, BK = 16;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+};
+// FP64: v_mfma_f64_16x16x4f64, a wave owns 64 x 64 outputs as 4 x 4 blocks
+// (a larger tile would double the 128-register accumulator).
+template <> struct mfma_cfg<double, false> {
+    static constexpr int BLK = 16, LG = 4, NI = 4, NJ = 4, BK = 16;
     using acc_t = f64x4;
     static constexpr int NACC = 4;
+    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
 };
 
 __device__ inline f32x16 mfma_op(float a, float b, f32x16 c)
@@ -247,7 +266,7 @@ template <typename R> struct vec16;
 template <> struct vec16<float> { using type = f32x4; static constexpr int N = 4; };
 template <> struct vec16<double> { using type = f64x2; static constexpr int N = 2; };
 
-constexpr int kBM = 128, kBN = 128;
+constexpr int kMaxBM = 256;    // largest workgroup tile height over the element types
 constexpr int kXcds = 8;        // XCDs of the GPU (round-robin workgroup placement)
 constexpr int64_t kGroupRows = 8;  // row tiles per group in the XCD-local tile order
 
@@ -272,15 +291,16 @@ struct GemmArgs {
     int64_t sAi, sAo, sBi, sBo, sCi, sCo;
 };
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool WIDE>
 __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 {
     using R = typename traits<T>::real;
-    using cfg = mfma_cfg<R>;
+    using cfg = mfma_cfg<R, WIDE>;
     using V16 = typename vec16<R>::type;
     constexpr int VN = vec16<R>::N;           // reals per 16 bytes
     constexpr bool CPX = traits<T>::is_complex;
-    constexpr int BLK = cfg::BLK, LG = cfg::LG, NBK = cfg::NB, BK = cfg::BK;
+    constexpr int BLK = cfg::BLK, LG = cfg::LG, NI = cfg::NI, NJ = cfg::NJ, BK = cfg::BK;
+    constexpr int kBM = cfg::BM, kBN = cfg::BN;
     constexpr int KS = BK / LG / (BK / (LG * VN)) ;  // k per lane group per 16-byte read = VN
     static_assert(KS == VN, "one 16-byte B read per lane group");
     constexpr int LDA_S = kBM + 4 / (int)(sizeof(R) / 4);   // As[k][i] row stride (+16 bytes)
@@ -291,8 +311,8 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wi = (wave & 1) * 64;   // wave's row offset inside the tile (i)
-    const int wj = (wave >> 1) * 64;  // wave's column offset (j)
+    const int wi = (wave & 1) * (NI * BLK);   // wave's row offset inside the tile (i)
+    const int wj = (wave >> 1) * (NJ * BLK);  // wave's column offset (j)
     // Tile of this workgroup. Workgroups are dealt to the 8 XCDs round-robin
     // by linear id, and each XCD has its own L2; for a single product the
     // ids are renumbered so that every XCD gets a contiguous range, walked in
@@ -456,11 +476,11 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
         else return lg + 4 * r;
     };
 
-    typename cfg::acc_t acc[NBK][NBK];
+    typename cfg::acc_t acc[NJ][NI];
 #pragma unroll
-    for (int b = 0; b < NBK; ++b)
+    for (int b = 0; b < NJ; ++b)
 #pragma unroll
-        for (int a = 0; a < NBK; ++a)
+        for (int a = 0; a < NI; ++a)
 #pragma unroll
             for (int r = 0; r < cfg::NACC; ++r) acc[b][a][r] = 0;
 
@@ -483,18 +503,18 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
         // full wait per MFMA group). LDS returns in order, so the MFMAs start
         // as soon as their own fragments have arrived.
         constexpr int NQ = BK / (LG * VN);
-        V16 bv[NQ][NBK];
-        R av[NQ][VN][NBK];
+        V16 bv[NQ][NJ];
+        R av[NQ][VN][NI];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int kq = q * LG * VN + lg * VN;  // this lane group's first k in the group
 #pragma unroll
-            for (int b = 0; b < NBK; ++b)
+            for (int b = 0; b < NJ; ++b)
                 bv[q][b] = *(const V16 *)&bs[(wj + b * BLK + lrow) * LDB_S + kq];
 #pragma unroll
             for (int s = 0; s < VN; ++s)
 #pragma unroll
-                for (int a = 0; a < NBK; ++a) av[q][s][a] = as[(kq + s) * LDA_S + wi + a * BLK + lrow];
+                for (int a = 0; a < NI; ++a) av[q][s][a] = as[(kq + s) * LDA_S + wi + a * BLK + lrow];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -502,9 +522,9 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 #pragma unroll
             for (int s = 0; s < VN; ++s)
 #pragma unroll
-                for (int b = 0; b < NBK; ++b)
+                for (int b = 0; b < NJ; ++b)
 #pragma unroll
-                    for (int a = 0; a < NBK; ++a)
+                    for (int a = 0; a < NI; ++a)
                         acc[b][a] = mfma_op(bv[q][b][s], av[q][s][a], acc[b][a]);
         __builtin_amdgcn_sched_barrier(0);
         if (st + 1 < nsteps) store_step(buf ^ 1, PF == 2 ? ((st + 1) & 1) : 0);
@@ -513,9 +533,9 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 
     // ---- epilogue: acc[b][a] holds D[j][i] for j in block b, i in block a ----
 #pragma unroll
-    for (int b = 0; b < NBK; ++b)
+    for (int b = 0; b < NJ; ++b)
 #pragma unroll
-        for (int a = 0; a < NBK; ++a)
+        for (int a = 0; a < NI; ++a)
 #pragma unroll
             for (int r = 0; r < cfg::NACC; ++r) {
                 const int64_t i = i0 + wi + a * BLK + lrow;
@@ -566,6 +586,13 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
         p.alpha = alpha;
         p.cscale = beta / alpha;
     }
+    // the wide f32 tile for large full products: K of 2048 or more and at
+    // least two wide tiles per CU (a triangular product keeps the finer
+    // tiles, which balance its uneven rows better)
+    using CW = mfma_cfg<R, std::is_same<R, float>::value>;
+    const bool wide = std::is_same<R, float>::value && !a_lower && p.Kr >= 2048 &&
+                      ((p.Mr + CW::BM - 1) / CW::BM) * ((N + CW::BN - 1) / CW::BN) * batch >= 512;
+    const int64_t kBM = wide ? CW::BM : mfma_cfg<R>::BM, kBN = wide ? CW::BN : mfma_cfg<R>::BN;
     const int64_t gx = (p.Mr + kBM - 1) / kBM;
     const int64_t gy = (N + kBN - 1) / kBN;
     if (gx > 0x7fffffff || gy > 65535 || batch > 65535) return hipErrorInvalidConfiguration;
@@ -575,8 +602,15 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
                      (ldb * sz) % 16 == 0 && (sAi * sz) % 16 == 0 && (sAo * sz) % 16 == 0 &&
                      (sBi * sz) % 16 == 0 && (sBo * sz) % 16 == 0;
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)batch);
-    if (vec) hipLaunchKernelGGL((gemm_kernel<T, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((gemm_kernel<T, false>), grid, dim3(256), 0, s, p);
+    if constexpr (std::is_same<R, float>::value) {
+        if (wide) {
+            if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, true>), grid, dim3(256), 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<T, false, true>), grid, dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, false>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_kernel<T, false, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -639,6 +673,8 @@ template <typename T>
 int64_t splitk_chunks(int64_t M, int64_t N, int64_t K, int64_t part_elems)
 {
     const int64_t f = traits<T>::is_complex ? 2 : 1;
+    constexpr int64_t kBM = mfma_cfg<typename traits<T>::real>::BM;
+    constexpr int64_t kBN = mfma_cfg<typename traits<T>::real>::BN;
     const int64_t tiles = ((M * f + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     if (tiles >= 256 || K < 2 * kSplitMinChunk || M * N <= 0) return 1;
     int64_t S = (kSplitTarget + tiles - 1) / tiles;
@@ -653,7 +689,7 @@ int64_t splitk_part_elems(int64_t m, int64_t n)
     // partials of at most kSplitTarget tiles' worth of rows (plus one tile
     // of rounding) for n <= 256; larger n has enough tiles
     if (n > 256) return 0;
-    const int64_t rows = (int64_t)kSplitTarget * kBM + 16 * (int64_t)kBM;
+    const int64_t rows = (int64_t)kSplitTarget * kMaxBM + 16 * (int64_t)kMaxBM;
     return (rows < 16 * m ? rows : 16 * m) * n;
 }
 
