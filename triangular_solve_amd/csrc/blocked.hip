@@ -245,7 +245,7 @@ template <> struct mfma_cfg<float, true> {
 // FP64: v_mfma_f64_16x16x4f64, a wave owns 64 x 64 outputs as 4 x 4 blocks
 // (a larger tile would double the 128-register accumulator).
 template <> struct mfma_cfg<double, false> {
-    static constexpr int BLK = 16, LG = 4, NI = 4, NJ = 4, BK = 16;
+    static constexpr int BLK = 16, LG = 4, NI = 4, NJ = 4, BK = 8;
     using acc_t = f64x4;
     static constexpr int NACC = 4;
     static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
