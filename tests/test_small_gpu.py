@@ -226,19 +226,47 @@ def test_solve_tri_strided_views(hs, n, sA1, pa2, pa3):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_repeat_runs_bitwise_identical(hs, dtype):
-    """Race detector: the kernels are deterministic, so any run-to-run difference is a race."""
+    """Race detector: the kernels are deterministic, so any run-to-run
+    difference is a race. 1000 runs of each path (small regime in both
+    kernels, the 64 < m <= 256 band, the blocked path with split products),
+    each compared with the first bit for bit on the device."""
     import torch
-    for (m, n) in [(64, 64), (64, 10), (37, 6)]:
-        say("repeat", dtype, m, n)
-        A, B = colmajor_inputs(dtype, m, n, 16, seed=21)
+    cases = [(64, 64, 16, None), (64, 10, 16, None), (37, 6, 16, None), (150, 64, 8, None),
+             (300, 40, 1, 128), (1024, 16, 1, 256)]
+    for (m, n, batch, nb) in cases:
+        say("repeat x1000", dtype, m, n, batch, nb)
+        A, B = colmajor_inputs(dtype, m, n, batch, seed=21)
         dA, dB0 = to_dev(A), to_dev(B)
-        f = hs.entry("strided_batched", dtype)
-        outs = []
-        for it in range(100):
-            dB = dB0.clone()
-            assert f(m, n, 1.0, dA, m, m * m, dB, m, m * n, 16) == hs.SUCCESS
-            outs.append(dB)
+        dB = torch.empty_like(dB0)
+        ref = None
+        for it in range(1000):
+            dB.copy_(dB0)
+            if nb is None:
+                st = hs.entry("strided_batched", dtype)(m, n, 1.0, dA, m, m * m, dB, m, m * n, batch)
+            else:
+                st = hs.entry("ex", dtype)(m, n, 1.0, dA, m, dB, m, {"nb": nb, "path": hs.PATH_BLOCKED})
+            assert st == hs.SUCCESS
+            if ref is None:
+                ref = dB.clone()
+            else:   # raw bits, so NaN compares too
+                assert torch.equal(dB.view(torch.uint8), ref.view(torch.uint8)), (m, n, it)
         torch.cuda.synchronize()
-        ref = outs[0].cpu().numpy().view(np.uint8)
-        for o in outs[1:]:
-            assert np.array_equal(o.cpu().numpy().view(np.uint8), ref)
+
+
+def test_repeat_solve_tri_bitwise_identical(hs):
+    """The SOLVE_TRI kernels (one wave per group of right-hand sides, and the
+    two-wave 128-row kernel), 1000 runs each, bit for bit."""
+    import torch
+    for n, k, e2, e3 in [(64, 6, 4, 2), (64, 10, 2, 2), (128, 8, 4, 1)]:
+        A = synth.tri("f32", n, e2 * e3, seed=5, offdiag_div=n, layout="row")
+        B = synth.rhs("f32", n, k, e2 * e3, seed=6, layout="row")
+        dA, dB = to_dev(A), to_dev(B)
+        dX = torch.empty_like(dB)
+        args = (n, k, dA, dB, dX, e2, e3, n, n * n, e2 * n * n, k, n * k, e2 * n * k, k, n * k, e2 * n * k)
+        assert hs.hsma_solve_tri_f32(*args) == hs.SUCCESS
+        ref = dX.clone()
+        for it in range(1000):
+            dX.fill_(7.0)
+            assert hs.hsma_solve_tri_f32(*args) == hs.SUCCESS
+            assert torch.equal(dX.view(torch.uint8), ref.view(torch.uint8)), (n, k, it)
+        torch.cuda.synchronize()
