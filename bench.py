@@ -340,7 +340,7 @@ def bench_variants(hs, torch, m=8192, dtypes=("f32", "f64"), runs=2, nvec=8):
     return out
 
 
-def bench_inversion(hs, torch, cases=((8192, 2048), (8192, 1024), (1024, 256), (1024, 128)),
+def bench_inversion(hs, torch, cases=((8192, 2048), (8192, 1024), (2048, 512), (1024, 256), (1024, 128)),
                     dtypes=DTYPES, runs=5):
     """The diagonal-block inversion alone, per route (blocked-inverse formula
     from 64 x 64 sub-blocks; fused 2*I_B blocks in LDS then merges; column

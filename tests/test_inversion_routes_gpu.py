@@ -106,3 +106,25 @@ def test_route_checks(hs):
     assert hs.hsma_diag_inv_ex_d(512, {"nb": 128, "inv": 9}, BAD, 512, BAD) == hs.INVALID_VALUE
     assert hs.hsma_trsm_ex_d(2048, 4, 1, BAD, 2048, BAD, 2048,
                              {"nb": 2048, "inv": hs.INV_COLUMN}) == hs.INVALID_VALUE
+
+
+@pytest.mark.parametrize("dt,m,nb,auto_is", [("f64", 1024, 256, "column"), ("f32", 1024, 256, "blocked"),
+                                               ("f64", 1024, 512, "blocked"), ("c128", 1024, 512, "column"),
+                                               ("c64", 2048, 512, "blocked")])
+def test_each_route_runs_its_own_arithmetic(hs, dt, m, nb, auto_is):
+    """An explicit route is the route that runs (the three give results that
+    differ in rounding), and AUTO is bitwise the route it is documented to
+    take for this dtype and block size."""
+    import torch
+    dA = to_dev(synth.tri(dt, m, seed=3))
+    nt = m // nb
+    got = {}
+    for name, o in routes(hs, dt, nb) + [("auto", {"inv": hs.INV_AUTO})]:
+        say("route dispatch", dt, m, nb, name)
+        dI = torch.zeros(nt * nb * nb, device="cuda", dtype=getattr(torch, TORCH[dt]))
+        assert hs.entry("diag_inv_ex", dt)(m, dict(o, nb=nb), dA, m, dI) == hs.SUCCESS, name
+        torch.cuda.synchronize()
+        got[name] = dI.cpu().numpy()
+    assert not np.array_equal(got["blocked"], got["column"])
+    assert not np.array_equal(got["blocked"], got["fused32"])
+    assert np.array_equal(got["auto"], got[auto_is])

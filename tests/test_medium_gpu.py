@@ -102,3 +102,57 @@ def test_batch_member_equals_solo_solve(hs, dtype, m, n):
             torch.cuda.synchronize()
             solo = dB2.cpu().numpy()[1]
         assert np.array_equal(dB.cpu().numpy()[p], solo)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("m,n", [(30, 5), (65, 1), (128, 64), (200, 300), (256, 17)])
+def test_rows64_route_single_problem(hs, dtype, m, n):
+    """The block-rows-of-64 route asked for by name on one problem (and on
+    m <= 64, where it is one block row), with alpha and padded leading
+    dimensions, against the oracle; rows below m stay untouched."""
+    import torch
+    cplx = dtype.startswith("c")
+    alpha = 1.5 - 0.25j if cplx else 0.75
+    lda, ldb = m + 3, m + 5
+    say("rows64 single", dtype, m, n)
+    A, B = colmajor_inputs(dtype, m, n, 1, lda=lda, ldb=ldb, seed=31 + m + n)
+    dA, dB = to_dev(A), to_dev(B)
+    st = hs.entry("ex", dtype)(m, n, alpha, dA, lda, dB, ldb, {"path": hs.PATH_ROWS64})
+    torch.cuda.synchronize()
+    assert st == hs.SUCCESS, hs.status_string(st)
+    X = dB.cpu().numpy()
+    Av, Bv = views(A, B, m)
+    assert rel_err(X[:, :, :m].transpose(0, 2, 1), oracle.trsm(Av, Bv, alpha)) <= TOL_LARGE[dtype]
+    assert np.array_equal(X[:, :, m:], B[:, :, m:])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_rows64_single_equals_batch_member(hs, dtype):
+    """One problem through the block-rows route gives bitwise the result it
+    gets as a member of a strided batch (which always takes that route)."""
+    import torch
+    m, n, batch = 177, 40, 4
+    A, B = colmajor_inputs(dtype, m, n, batch, seed=77)
+    dA, dB = to_dev(A), to_dev(B)
+    assert hs.entry("strided_batched", dtype)(m, n, 1.0, dA, m, m * m, dB, m, m * n, batch) == hs.SUCCESS
+    dA1, dB1 = to_dev(A[2:3]), to_dev(B[2:3])
+    assert hs.entry("ex", dtype)(m, n, 1.0, dA1, m, dB1, m, {"path": hs.PATH_ROWS64}) == hs.SUCCESS
+    torch.cuda.synchronize()
+    assert np.array_equal(dB.cpu().numpy()[2], dB1.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_single_problem_auto_route(hs, dtype):
+    """AUTO on one problem with 64 < m <= 256 takes the block-rows route for
+    n <= 32 and the blocked path above that (bitwise the explicit routes)."""
+    import torch
+    m = 177
+    f = hs.entry("ex", dtype)
+    for n, want in ((20, hs.PATH_ROWS64), (32, hs.PATH_ROWS64), (33, hs.PATH_BLOCKED)):
+        say("single auto route", dtype, m, n)
+        A, B = colmajor_inputs(dtype, m, n, 1, seed=n)
+        dA, dB1, dB2 = to_dev(A), to_dev(B), to_dev(B)
+        assert f(m, n, 1.0, dA, m, dB1, m, {"path": hs.PATH_AUTO}) == hs.SUCCESS
+        assert f(m, n, 1.0, dA, m, dB2, m, {"path": want}) == hs.SUCCESS
+        torch.cuda.synchronize()
+        assert np.array_equal(dB1.cpu().numpy(), dB2.cpu().numpy()), n

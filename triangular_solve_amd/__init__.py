@@ -32,7 +32,7 @@ SIDE = {"L": 0, "R": 1}
 UPLO = {"L": 0, "U": 1}
 OP = {"N": 0, "T": 1, "C": 2}
 DIAG = {"N": 0, "U": 1}
-PATH_AUTO, PATH_SMALL, PATH_BLOCKED = 0, 1, 2
+PATH_AUTO, PATH_SMALL, PATH_BLOCKED, PATH_ROWS64 = 0, 1, 2, 3
 INV_AUTO, INV_BLOCKED, INV_FUSED, INV_COLUMN = 0, 1, 2, 3
 
 # Phase codes of the blocked path's timing events (hsma_trsm_opts.events).

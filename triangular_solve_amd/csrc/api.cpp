@@ -173,12 +173,15 @@ hsma_status hip_status(hipError_t e)
 
 int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
 
+constexpr int64_t kMediumMaxM = 256;   // largest m of the block-rows-of-64 route
+
 hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
 {
     if (!o) return HSMA_STATUS_SUCCESS;
-    if (o->path < HSMA_PATH_AUTO || o->path > HSMA_PATH_BLOCKED) return HSMA_STATUS_INVALID_VALUE;
+    if (o->path < HSMA_PATH_AUTO || o->path > HSMA_PATH_ROWS64) return HSMA_STATUS_INVALID_VALUE;
     if (o->inv < HSMA_INV_AUTO || o->inv > HSMA_INV_COLUMN) return HSMA_STATUS_INVALID_VALUE;
     if (o->path == HSMA_PATH_SMALL && m > 64) return HSMA_STATUS_INVALID_VALUE;
+    if (o->path == HSMA_PATH_ROWS64 && m > kMediumMaxM) return HSMA_STATUS_INVALID_VALUE;
     if (o->nb != 0 && (!valid_nb(o->nb) || !nb_fits(o->nb, m, dtype)))
         return HSMA_STATUS_INVALID_VALUE;
     if (o->ib != 0) {
@@ -196,7 +199,12 @@ hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
 // (X_r = A_rr^{-1} (B_r - A[r, <r] X_<r)), the update by one strided-batched
 // matrix-core GEMM and the diagonal solve by the small regime, both over all
 // problems; 2 * ceil(m/64) launches instead of a blocked solve per problem.
-constexpr int64_t kMediumMaxM = 256;
+// A single problem of that size takes this route too when it has at most
+// kRows64MaxRhs right-hand sides: with few columns the blocked path's
+// inversion costs more than the substitution it replaces (measured on
+// MI355X, 1.1-3x for n <= 16 in all four types); with more columns the
+// inverse-times-block products of the blocked path win.
+constexpr int64_t kRows64MaxRhs = 32;
 
 template <typename T>
 hipError_t medium_batched(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
@@ -247,7 +255,8 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     const int path = opts ? opts->path : HSMA_PATH_AUTO;
     const bool small = path == HSMA_PATH_SMALL || (path == HSMA_PATH_AUTO && m <= 64);
     if (small) return hip_status(small_path<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
-    if (path == HSMA_PATH_AUTO && batch > 1 && m <= kMediumMaxM)
+    if (path == HSMA_PATH_ROWS64 ||
+        (path == HSMA_PATH_AUTO && m <= kMediumMaxM && (batch > 1 || n <= kRows64MaxRhs)))
         return hip_status(medium_batched<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
 
     // Blocked path.

@@ -66,9 +66,11 @@ __global__ void __launch_bounds__(256) diag_inv_kernel(const T *__restrict__ A, 
 #pragma unroll
     for (int q = 0; q < R; ++q) {
         const int i = tid * R + q;
-        inv[q] = (i < rb) ? recip(D[i + (int64_t)i * lda]) : one;
+        T d = one;
+        if (i < rb) d = D[i + (int64_t)i * lda];
+        inv[q] = recip(d);
 #pragma unroll
-        for (int c = 0; c < G; ++c) w[q][c] = (i == cstart + c) ? one : zero_of(T());
+        for (int c = 0; c < G; ++c) w[q][c] = pick(i == cstart + c, one, zero_of(T()));
     }
 
     // Column k of D_t below the diagonal, as this thread's rows see it;
@@ -119,7 +121,7 @@ __global__ void __launch_bounds__(256) diag_inv_kernel(const T *__restrict__ A, 
 #pragma unroll
                 for (int c = 0; c < G; ++c) {
                     const T u = fms(w[q][c], dcur[q][kk], y[c]);
-                    w[q][c] = below ? u : w[q][c];
+                    w[q][c] = pick(below, u, w[q][c]);
                 }
             }
         }
@@ -164,16 +166,18 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
 template <typename T>
 static bool blocked_inverse_applies(int64_t m, int nb);
 template <typename T>
+static bool auto_merges(int64_t m, int nb);
+template <typename T>
 bool invert_route_applies(int64_t m, int nb, int ib, int route);
-// Inversion of all diagonal blocks: the blocked-inverse formula where it
-// applies (temporaries allocated stream-ordered), else diag_inv_kernel.
+// Inversion of all diagonal blocks by route: with merge products
+// (temporaries allocated stream-ordered) or by diag_inv_kernel alone.
 template <typename T>
 hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA,
                            hipStream_t s, int route)
 {
     if (!invert_route_applies<T>(m, nb, ib, route)) return hipErrorInvalidValue;
     const bool merges = route == HSMA_INV_FUSED || route == HSMA_INV_BLOCKED ||
-                        (route == HSMA_INV_AUTO && blocked_inverse_applies<T>(m, nb));
+                        (route == HSMA_INV_AUTO && auto_merges<T>(m, nb));
     if (!merges) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
     void *tmp = nullptr;
     hipError_t e = workspace_alloc(&tmp, (size_t)blocked_inverse_temp_elems(m, nb) * sizeof(T), s);
@@ -757,6 +761,19 @@ static bool blocked_inverse_applies(int64_t m, int nb)
     return m % nb == 0 && nb % 64 == 0 && nb >= 128;
 }
 
+// What HSMA_INV_AUTO takes: the blocked-inverse formula where it applies,
+// except for blocks of at most 256 in f64 and c64 (512 in c128), where one
+// column substitution launch measured faster on MI355X than the small
+// solves plus log2(nb / 64) rounds of merge products (whose fixed cost
+// dominates there).
+template <typename T>
+static bool auto_merges(int64_t m, int nb)
+{
+    if (!blocked_inverse_applies<T>(m, nb)) return false;
+    if (std::is_same<T, float>::value) return true;
+    return nb > (sizeof(T) == 16 ? 512 : 256);
+}
+
 template <typename T>
 static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T *invA, T *temp,
                                   hipStream_t s)
@@ -803,7 +820,8 @@ static hipError_t blocked_inverse(int64_t m, int nb, const T *A, int64_t lda, T 
 // one workgroup holds a whole 2I_B x 2I_B diagonal block in LDS -- the
 // paper's 4 I_B^2 elements, which caps I_B at 64 (32 for double complex) on
 // gfx950's 160 KB -- inverts its two I_B x I_B diagonal blocks by
-// substitution against identity columns (one lane per column), then forms
+// substitution against identity columns (one lane per row, the columns in
+// registers, rows broadcast with v_readlane), then forms
 // the off-diagonal block of the inverse, -L22^{-1} L21 L11^{-1}, with two
 // small products in LDS (T = L21 L11^{-1} kept in the otherwise unused upper
 // right quarter). Larger blocks are then merged by the batched products of
@@ -833,25 +851,35 @@ __global__ void __launch_bounds__(256) fused_inv_kernel(const T *__restrict__ A,
     }
     __syncthreads();
 
-    // (1) L11^{-1} and L22^{-1}: thread (q, c) solves L_qq y = e_c
-    if (tid < S2) {
-        const int q = tid / IB, c = tid % IB, o = q * IB;
-        T y[IB];
+    // (1) L11^{-1} and L22^{-1} by substitution against identity columns.
+    // Wave w takes diagonal block q = w / 2 and half of its columns; lane i
+    // holds row i of those columns in registers. Step j finishes row j
+    // (scaled by 1/l_jj, exact zero left of the diagonal), broadcasts it with
+    // v_readlane and the rows below subtract l_ij times it. Only the loop
+    // over columns is unrolled, so no register array is indexed by j.
+    {
+        constexpr int NC = IB / 2;
+        const int wave = tid >> 6, lane = tid & 63;
+        const int o = (wave >> 1) * IB, cb = (wave & 1) * NC;
+        T w[NC];
 #pragma unroll
-        for (int i = 0; i < IB; ++i) y[i] = i == c ? one : zero_of(T());
-#pragma unroll
+        for (int c = 0; c < NC; ++c) w[c] = pick(lane == cb + c, one, zero_of(T()));
         for (int j = 0; j < IB; ++j) {
             const T r = recip(S[(o + j) * LD + o + j]);
-            y[j] = j >= c ? mul(y[j], r) : zero_of(T());   // exact zeros above the diagonal
+            T a = zero_of(T());
+            if (lane < IB) a = S[(o + j) * LD + o + lane];   // l_ij of this block
+            const bool below = lane > j, at = lane == j;
 #pragma unroll
-            for (int i = j + 1; i < IB; ++i) y[i] = fms(y[i], S[(o + j) * LD + o + i], y[j]);
+            for (int c = 0; c < NC; ++c) {
+                const T x = pick(j >= cb + c, mul(readlane(w[c], j), r), zero_of(T()));
+                w[c] = pick(below, fms(w[c], a, x), pick(at, x, w[c]));
+            }
         }
-        // every lane has read its block's coefficients before any overwrites them
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        __syncthreads();   // every coefficient read before the inverse overwrites them
+        if (lane < IB) {
 #pragma unroll
-        for (int i = 0; i < IB; ++i) S[(o + c) * LD + o + i] = y[i];
+            for (int c = 0; c < NC; ++c) S[(o + cb + c) * LD + o + lane] = w[c];
+        }
     }
     __syncthreads();
 
@@ -1018,8 +1046,9 @@ hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T 
     if (!invert_route_applies<T>(m, nb, ib, route)) return hipErrorInvalidValue;
     if (route == HSMA_INV_FUSED) return fused_inverse<T>(m, nb, ib, A, lda, invA, temp, s);
     if (route == HSMA_INV_COLUMN) return diag_invert<T>(m, nb, ib, A, lda, invA, s);
-    return blocked_inverse_applies<T>(m, nb) ? blocked_inverse<T>(m, nb, A, lda, invA, temp, s)
-                                             : diag_invert<T>(m, nb, ib, A, lda, invA, s);
+    if (route == HSMA_INV_BLOCKED || (route == HSMA_INV_AUTO && auto_merges<T>(m, nb)))
+        return blocked_inverse<T>(m, nb, A, lda, invA, temp, s);
+    return diag_invert<T>(m, nb, ib, A, lda, invA, s);
 }
 
 template <typename T>

@@ -99,7 +99,18 @@ __device__ inline cplx<R> recip(cplx<R> d)
     const R r = q / p;
     const R t = R(1) / fmaR(q, r, p);
     const R u = r * t;
-    return sw ? cplx<R>{u, -t} : cplx<R>{t, -u};
+    return {sw ? u : t, sw ? -t : -u};
+}
+
+// c ? a : b on values, component by component for complex types. A
+// conditional expression whose operands are complex lvalues selects between
+// their addresses, which can keep a register array in scratch memory.
+__device__ inline float pick(bool c, float a, float b) { return c ? a : b; }
+__device__ inline double pick(bool c, double a, double b) { return c ? a : b; }
+template <typename R>
+__device__ inline cplx<R> pick(bool c, cplx<R> a, cplx<R> b)
+{
+    return {c ? a.re : b.re, c ? a.im : b.im};
 }
 
 // ---- cross-lane broadcast of a wave-uniform lane index (v_readlane) --------

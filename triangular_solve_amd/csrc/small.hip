@@ -90,7 +90,9 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
     // diagonal reads the constant one instead (stride 0).
     const T *dg = p.unit ? unit_one<T>() : Ab;
     const int64_t sdg = p.unit ? 0 : p.sai + p.saj;
-    const T inv = recip(lane < m ? dg[lane * sdg] : one);
+    T d = one;
+    if (lane < m) d = dg[lane * sdg];
+    const T inv = recip(d);
 
     if constexpr (RR) {
         static_assert(!traits<T>::is_complex, "row registers for real types only");
@@ -122,7 +124,7 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
 #pragma unroll
             for (int q = 0; q < KW; ++q) {
                 const T u = fms(w[q], a[j], readlane(w[q], j));
-                w[q] = below ? u : w[q];
+                w[q] = pick(below, u, w[q]);
             }
         }
 #pragma unroll
@@ -170,7 +172,7 @@ __global__ void __launch_bounds__(256) rowlane_kernel(RowlaneArgs<T> p)
         for (int q = 0; q < KW; ++q) {
             const T x = readlane(w[q], j);
             const T u = fms(w[q], a, x);
-            w[q] = below ? u : w[q];
+            w[q] = pick(below, u, w[q]);
         }
     };
     if (m == 64) {
