@@ -1,5 +1,6 @@
 """Build libhsma_trsm.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -34,12 +35,41 @@ def _compile(src, incremental=False):
         newest = max(os.path.getmtime(os.path.join(CSRC, src)), _deps_mtime())
         if os.path.getmtime(obj) > newest:
             return obj, []
-    cmd = ["hipcc"] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    # the compiler's per-kernel resource remarks (registers, scratch,
+    # occupancy) go to <object>.resources.txt next to the object
+    cmd = ["hipcc"] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c",
+                               os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-8000:]))
-    warn = [l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    remarks = [l for l in r.stderr.splitlines() if "kernel-resource-usage" in l]
+    with open(obj + ".resources.txt", "w") as f:
+        f.write("\n".join(remarks) + "\n")
+    warn = [l for l in r.stderr.splitlines()
+            if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l and l.strip()]
     return obj, warn
+
+
+def kernel_resources():
+    """{kernel symbol: {"VGPRs", "AGPRs", "ScratchSize" (bytes per lane),
+    "Occupancy" (waves per SIMD), "VGPRsSpill", "SGPRsSpill": int}}
+    from the remarks of the last build of every source."""
+    out = {}
+    for src in SOURCES:
+        path = os.path.join(BUILD, os.path.basename(src) + ".o.resources.txt")
+        if not os.path.exists(path):
+            continue
+        cur = None
+        for line in open(path):
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                cur = out.setdefault(m.group(1), {})
+                continue
+            m = re.search(r"remark: \s*(VGPRs Spill|SGPRs Spill|VGPRs|AGPRs|ScratchSize|Occupancy)"
+                          r"(?: \[[^]]*\])?: (\d+)", line)
+            if m and cur is not None:
+                cur[m.group(1).replace(" ", "")] = int(m.group(2))
+    return out
 
 
 def build(verbose=False, incremental=False):
