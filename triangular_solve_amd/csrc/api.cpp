@@ -74,6 +74,28 @@ hipError_t workspace_alloc(void **p, size_t bytes, hipStream_t s)
 hipError_t workspace_free(void *p, hipStream_t s) { return hipFreeAsync(p, s); }
 
 namespace {
+hipStream_t g_aux[kMaxDevices] = {};
+std::mutex g_aux_mutex;
+}  // namespace
+
+hipError_t aux_stream(hipStream_t *out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_aux_mutex);
+    if (!g_aux[dev]) {
+        hipStream_t st = nullptr;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+        g_aux[dev] = st;
+    }
+    *out = g_aux[dev];
+    return hipSuccess;
+}
+
+namespace {
 
 // ---------------------------------------------------------------------------
 // Block-size table: tested shapes (m_i, n_i) and the best N_B at each, per

@@ -1064,7 +1064,7 @@ hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T 
 template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
                          T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec, T *part,
-                         int64_t part_elems)
+                         int64_t part_elems, const CopyOverlap *ov)
 {
     using R = typename traits<T>::real;
     const int64_t nt = (m + nb - 1) / nb;
@@ -1080,24 +1080,52 @@ hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, 
                                part, part_elems, s);
         if (e == hipSuccess) e = mark(HSMA_PHASE_COPY);
         if (e != hipSuccess) break;
+        // X_t into B_t: on the second stream when given, after W is ready
+        hipStream_t cs = s;
+        if (ov) {
+            e = hipEventRecord(ov->ready, s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(ov->aux, ov->ready, 0);
+            if (e != hipSuccess) break;
+            cs = ov->aux;
+        }
         for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += 65535) {
             const int64_t nc = n - c0 < 65535 ? n - c0 : 65535;
             hipLaunchKernelGGL(copy_kernel<T>, dim3((unsigned)((rb + 255) / 256), (unsigned)nc),
-                               dim3(256), 0, s, W + c0 * nb, (int64_t)nb, rb, B + r0 + c0 * ldb, ldb);
+                               dim3(256), 0, cs, W + c0 * nb, (int64_t)nb, rb, B + r0 + c0 * ldb, ldb);
             e = hipGetLastError();
         }
-        if (e != hipSuccess) break;
-        // B[below] -= A[below, t] X_t
-        if (r0 + rb < m) {
+        bool copy_pending = false;
+        if (ov) {
+            const hipError_t ew = hipEventRecord(ov->copied, ov->aux);
+            if (ew == hipSuccess) copy_pending = true;
+            else (void)hipStreamSynchronize(ov->aux);
+            if (e == hipSuccess) e = ew;
+        }
+        // B[below] -= A[below, t] X_t: reads W and writes only the rows below
+        // B_t, so it runs beside the copy
+        if (e == hipSuccess && r0 + rb < m) {
             e = mark(HSMA_PHASE_TRAILING);
             if (e == hipSuccess)
                 e = gemm_splitk<T>(m - r0 - rb, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb,
                                    R(1), B + r0 + rb, ldb, false, part, part_elems, s);
         }
+        // s does not go on to overwrite W (next block row) or finish before
+        // the copy has read it, also after a failure
+        if (copy_pending) {
+            const hipError_t ew = hipStreamWaitEvent(s, ov->copied, 0);
+            if (ew != hipSuccess) (void)hipStreamSynchronize(ov->aux);
+            if (e == hipSuccess) e = ew;
+        }
+        if (e != hipSuccess) break;
     }
     if (e == hipSuccess) e = mark(HSMA_PHASE_END);
     return e;
 }
+
+// Block rows of at least this many elements copy W -> B_t on the second
+// stream: on MI355X the copy of an m = n = 8192 solve (N_B = 2048) is 2 % of
+// it; below this size the event round trip costs about what it hides.
+constexpr int64_t kOverlapMinElems = int64_t(1) << 22;
 
 template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
@@ -1114,9 +1142,20 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     const int64_t part_elems = splitk_part_elems(m, n);
     hipError_t e = rec ? rec->mark(HSMA_PHASE_DIAG_INV, s) : hipSuccess;
     if (e == hipSuccess) e = blocked_invert<T>(m, nb, ib, A, lda, invA, W, s, route);
-    if (e == hipSuccess)
-        e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec, part_elems ? part : nullptr,
-                             part_elems);
+    if (e != hipSuccess) return e;
+    // Large block rows: the W -> B_t copies run on a second stream beside the
+    // trailing products (not when the caller times the phases on s)
+    CopyOverlap ov{};
+    const bool overlap = !rec && nt > 1 && (int64_t)nb * n >= kOverlapMinElems &&
+                         aux_stream(&ov.aux) == hipSuccess &&
+                         hipEventCreateWithFlags(&ov.ready, hipEventDisableTiming) == hipSuccess;
+    const bool overlap2 = overlap &&
+                          hipEventCreateWithFlags(&ov.copied, hipEventDisableTiming) == hipSuccess;
+    e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec, part_elems ? part : nullptr,
+                         part_elems, overlap2 ? &ov : nullptr);
+    // (events still pending are released by the runtime once they complete)
+    if (overlap) (void)hipEventDestroy(ov.ready);
+    if (overlap2) (void)hipEventDestroy(ov.copied);
     return e;
 }
 
@@ -1137,7 +1176,8 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     template hipError_t blocked_invert<T>(int64_t, int, int, const T *, int64_t, T *, T *,        \
                                           hipStream_t, int);                                      \
     template hipError_t blocked_apply<T>(int64_t, int64_t, int, const T *, int64_t, const T *, T *, \
-                                         int64_t, T *, hipStream_t, PhaseRec *, T *, int64_t);
+                                         int64_t, T *, hipStream_t, PhaseRec *, T *, int64_t,   \
+                                         const CopyOverlap *);
 HSMA_INST(float)
 HSMA_INST(double)
 HSMA_INST(c32)

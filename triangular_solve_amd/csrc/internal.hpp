@@ -118,11 +118,22 @@ template <typename T>
 hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *invA, T *temp,
                           hipStream_t s, int route = 0);
 // part (part_elems elements, may be NULL) holds split-K partial products
-// for products with few output tiles.
+// for products with few output tiles. With ov, each W -> B_t copy runs on
+// ov->aux beside the trailing product on s (both only read W), and s waits
+// for it before W is written again.
+struct CopyOverlap {
+    hipStream_t aux;
+    hipEvent_t ready, copied;
+};
 template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
                          T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec = nullptr,
-                         T *part = nullptr, int64_t part_elems = 0);
+                         T *part = nullptr, int64_t part_elems = 0,
+                         const CopyOverlap *ov = nullptr);
+
+// The second stream of the current device for the blocked path's copies
+// (created on first use, default priority, kept until the process ends).
+hipError_t aux_stream(hipStream_t *out);
 
 // Small-regime dispatch on column-major storage, in place (m <= 64): the
 // lane-per-column kernel needs the full 64 rows, enough columns to fill a
