@@ -226,11 +226,13 @@ hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *in
 
 // NI x NJ blocks of BLK x BLK outputs per wave (NI along the rows i of C, NJ
 // along its columns j), four waves as 2 x 2, so a workgroup tile is
-// BM = 2*NI*BLK rows by BN = 2*NJ*BLK columns; K steps of BK. WIDE selects
-// the tall f32 tile for large products.
-template <typename R, bool WIDE = false> struct mfma_cfg;
+// BM = 2*NI*BLK rows by BN = 2*NJ*BLK columns; K steps of BK. TILE selects
+// the standard tile, the tall f32 tile for large products or the 64 x 64
+// tile for products with few standard tiles.
+constexpr int kTileStd = 0, kTileWide = 1, kTileSmall = 2;
+template <typename R, int TILE = kTileStd> struct mfma_cfg;
 // FP32: v_mfma_f32_32x32x2f32, a wave owns 64 x 64 outputs as 2 x 2 blocks.
-template <> struct mfma_cfg<float, false> {
+template <> struct mfma_cfg<float, kTileStd> {
     static constexpr int BLK = 32, LG = 2, NI = 2, NJ = 2, BK = 32;  // LG: lane groups along k
     using acc_t = f32x16;
     static constexpr int NACC = 16;
@@ -240,16 +242,32 @@ template <> struct mfma_cfg<float, false> {
 // workgroup tile with K steps of 16: a third fewer LDS bytes per MFMA and
 // more flops per byte of L2 traffic. It wins on large products (the trailing
 // updates, K >= 2048) and loses where its coarser tiles leave CUs idle.
-template <> struct mfma_cfg<float, true> {
+template <> struct mfma_cfg<float, kTileWide> {
     static constexpr int BLK = 32, LG = 2, NI = 4, NJ = 2, BK = 16;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+};
+// FP32, small: a wave owns one 32 x 32 block, a 64 x 64 workgroup tile: four
+// times the workgroups of the standard tile for products that would leave
+// most CUs idle (the block-inverse merges, single problems in block rows).
+template <> struct mfma_cfg<float, kTileSmall> {
+    static constexpr int BLK = 32, LG = 2, NI = 1, NJ = 1, BK = 32;
     using acc_t = f32x16;
     static constexpr int NACC = 16;
     static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
 };
 // FP64: v_mfma_f64_16x16x4f64, a wave owns 64 x 64 outputs as 4 x 4 blocks
 // (a larger tile would double the 128-register accumulator).
-template <> struct mfma_cfg<double, false> {
+template <> struct mfma_cfg<double, kTileStd> {
     static constexpr int BLK = 16, LG = 4, NI = 4, NJ = 4, BK = 8;
+    using acc_t = f64x4;
+    static constexpr int NACC = 4;
+    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+};
+// FP64, small: a wave owns 32 x 32 outputs as 2 x 2 blocks, a 64 x 64 tile.
+template <> struct mfma_cfg<double, kTileSmall> {
+    static constexpr int BLK = 16, LG = 4, NI = 2, NJ = 2, BK = 8;
     using acc_t = f64x4;
     static constexpr int NACC = 4;
     static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
@@ -271,6 +289,7 @@ template <> struct vec16<float> { using type = f32x4; static constexpr int N = 4
 template <> struct vec16<double> { using type = f64x2; static constexpr int N = 2; };
 
 constexpr int kMaxBM = 256;    // largest workgroup tile height over the element types
+constexpr int64_t kSmallTileBelow = 256;  // standard-tile count under which the 64 x 64 tile runs
 constexpr int kXcds = 8;        // XCDs of the GPU (round-robin workgroup placement)
 constexpr int64_t kGroupRows = 8;  // row tiles per group in the XCD-local tile order
 
@@ -295,11 +314,11 @@ struct GemmArgs {
     int64_t sAi, sAo, sBi, sBo, sCi, sCo;
 };
 
-template <typename T, bool VEC, bool WIDE>
+template <typename T, bool VEC, int TILE>
 __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 {
     using R = typename traits<T>::real;
-    using cfg = mfma_cfg<R, WIDE>;
+    using cfg = mfma_cfg<R, TILE>;
     using V16 = typename vec16<R>::type;
     constexpr int VN = vec16<R>::N;           // reals per 16 bytes
     constexpr bool CPX = traits<T>::is_complex;
@@ -356,6 +375,8 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
     // A tile: BK x kBM reals = (kBM/VN) chunks per k row; chunks per thread:
     constexpr int A_CH = BK * kBM / VN / 256;
     constexpr int B_CH = BK * kBN / VN / 256;
+    static_assert(A_CH * 256 * VN == BK * kBM && B_CH * 256 * VN == BK * kBN,
+                  "the 256 threads' 16-byte chunks cover a K step's tiles exactly");
     // PF K steps of staging registers: step s+PF is fetched while step s is
     // multiplied (with PF = 2, s+1 already sits in the other LDS buffer).
     // Measured on MI355X, PF = 2 gained nothing over PF = 1, which needs
@@ -593,10 +614,17 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     // the wide f32 tile for large full products: K of 2048 or more and at
     // least two wide tiles per CU (a triangular product keeps the finer
     // tiles, which balance its uneven rows better)
-    using CW = mfma_cfg<R, std::is_same<R, float>::value>;
+    using CW = mfma_cfg<R, std::is_same<R, float>::value ? kTileWide : kTileStd>;
+    using CS = mfma_cfg<R, kTileStd>;
+    using CM = mfma_cfg<R, kTileSmall>;
     const bool wide = std::is_same<R, float>::value && !a_lower && p.Kr >= 2048 &&
                       ((p.Mr + CW::BM - 1) / CW::BM) * ((N + CW::BN - 1) / CW::BN) * batch >= 512;
-    const int64_t kBM = wide ? CW::BM : mfma_cfg<R>::BM, kBN = wide ? CW::BN : mfma_cfg<R>::BN;
+    // fewer standard tiles than CUs: the 64 x 64 tile (four times the
+    // workgroups of the same product)
+    const bool small = !wide && ((p.Mr + CS::BM - 1) / CS::BM) * ((N + CS::BN - 1) / CS::BN) * batch <
+                                    kSmallTileBelow;
+    const int64_t kBM = wide ? CW::BM : small ? CM::BM : CS::BM;
+    const int64_t kBN = wide ? CW::BN : small ? CM::BN : CS::BN;
     const int64_t gx = (p.Mr + kBM - 1) / kBM;
     const int64_t gy = (N + kBN - 1) / kBN;
     if (gx > 0x7fffffff || gy > 65535 || batch > 65535) return hipErrorInvalidConfiguration;
@@ -608,13 +636,18 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)batch);
     if constexpr (std::is_same<R, float>::value) {
         if (wide) {
-            if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, true>), grid, dim3(256), 0, s, p);
-            else hipLaunchKernelGGL((gemm_kernel<T, false, true>), grid, dim3(256), 0, s, p);
+            if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileWide>), grid, dim3(256), 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<T, false, kTileWide>), grid, dim3(256), 0, s, p);
             return hipGetLastError();
         }
     }
-    if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, false>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((gemm_kernel<T, false, false>), grid, dim3(256), 0, s, p);
+    if (small) {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileSmall>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<T, false, kTileSmall>), grid, dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
+    if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileStd>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_kernel<T, false, kTileStd>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
