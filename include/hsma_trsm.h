@@ -79,7 +79,7 @@ typedef struct { double re, im; } hsma_double_complex;
  *   alpha scalar applied to B before the solve
  *   A     device pointer, lda >= max(1, m); read-only, lower triangle only
  *   B     device pointer, ldb >= max(1, m); on return holds X
- * Route: m <= 64 the small regime (one launch); 64 < m <= 256 with n <= 32
+ * Route: m <= 64 the small regime (one launch); 64 < m <= 192 with n <= 16
  * block rows of 64 (as the strided-batched entry points below, no
  * workspace); otherwise the blocked solver.
  * Errors: INVALID_SIZE, INVALID_POINTER (A or B NULL with m*n > 0),
@@ -252,10 +252,10 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
  *         block rows of 64, each updated by one matrix-core GEMM with the
  *         finished rows and solved by the small regime, no inversion and no
  *         workspace; what AUTO takes for batches with 64 < m <= 256
- *         and for single problems with 64 < m <= 256 and n <= 32)
+ *         and for single problems with 64 < m <= 192 and n <= 16)
  *   inv   route of the diagonal-block inversion (blocked path):
  *         HSMA_INV_AUTO: BLOCKED where it applies (for f64 and c64 only
- *           when nb > 256, for c128 when nb > 512), else COLUMN;
+ *           when nb > 128, for c128 when nb > 256), else COLUMN;
  *         HSMA_INV_BLOCKED: 64 x 64 sub-blocks by substitution against
  *           identity columns, merged by the block-inverse formula in batched
  *           matrix-core products (m a multiple of nb, nb a multiple of 64,
@@ -332,7 +332,7 @@ hsma_status hsma_trsm_ex_z(int64_t m, int64_t n, hsma_double_complex alpha,
  * rows/columns beyond m in the last block, are written as exact zeros (the
  * padded part of the last block holds the identity on its diagonal).
  * nb, ib as in hsma_trsm_opts (0 = defaults). When m is a multiple of nb and
- * nb a multiple of 64 with nb >= 128 (f64 and c64: nb > 256; c128: nb > 512;
+ * nb a multiple of 64 with nb >= 128 (f64 and c64: nb > 128; c128: nb > 256;
  * where this measured faster than the column route), 64 x 64 sub-blocks are inverted by
  * substitution against identity columns and merged by the block-inverse
  * formula with matrix-core products (ib unused; a temporary of nb*nb/4

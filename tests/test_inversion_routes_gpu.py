@@ -108,8 +108,9 @@ def test_route_checks(hs):
                              {"nb": 2048, "inv": hs.INV_COLUMN}) == hs.INVALID_VALUE
 
 
-@pytest.mark.parametrize("dt,m,nb,auto_is", [("f64", 1024, 256, "column"), ("f32", 1024, 256, "blocked"),
-                                               ("f64", 1024, 512, "blocked"), ("c128", 1024, 512, "column"),
+@pytest.mark.parametrize("dt,m,nb,auto_is", [("f64", 1024, 128, "column"), ("f32", 1024, 256, "blocked"),
+                                               ("f64", 1024, 256, "blocked"), ("c128", 1024, 256, "column"),
+                                               ("c128", 1024, 512, "blocked"), ("c64", 1024, 128, "column"),
                                                ("c64", 2048, 512, "blocked")])
 def test_each_route_runs_its_own_arithmetic(hs, dt, m, nb, auto_is):
     """An explicit route is the route that runs (the three give results that

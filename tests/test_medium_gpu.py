@@ -143,16 +143,16 @@ def test_rows64_single_equals_batch_member(hs, dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_single_problem_auto_route(hs, dtype):
-    """AUTO on one problem with 64 < m <= 256 takes the block-rows route for
-    n <= 32 and the blocked path above that (bitwise the explicit routes)."""
+    """AUTO on one problem takes the block-rows route for 64 < m <= 192 with
+    n <= 16 and the blocked path otherwise (bitwise the explicit routes)."""
     import torch
-    m = 177
     f = hs.entry("ex", dtype)
-    for n, want in ((20, hs.PATH_ROWS64), (32, hs.PATH_ROWS64), (33, hs.PATH_BLOCKED)):
+    for m, n, want in ((177, 1, hs.PATH_ROWS64), (177, 16, hs.PATH_ROWS64), (192, 9, hs.PATH_ROWS64),
+                       (177, 17, hs.PATH_BLOCKED), (193, 4, hs.PATH_BLOCKED), (256, 1, hs.PATH_BLOCKED)):
         say("single auto route", dtype, m, n)
         A, B = colmajor_inputs(dtype, m, n, 1, seed=n)
         dA, dB1, dB2 = to_dev(A), to_dev(B), to_dev(B)
         assert f(m, n, 1.0, dA, m, dB1, m, {"path": hs.PATH_AUTO}) == hs.SUCCESS
         assert f(m, n, 1.0, dA, m, dB2, m, {"path": want}) == hs.SUCCESS
         torch.cuda.synchronize()
-        assert np.array_equal(dB1.cpu().numpy(), dB2.cpu().numpy()), n
+        assert np.array_equal(dB1.cpu().numpy(), dB2.cpu().numpy()), (m, n)

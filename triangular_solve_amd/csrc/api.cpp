@@ -221,12 +221,13 @@ hsma_status check_opts(const hsma_trsm_opts *o, int dtype, int64_t m)
 // (X_r = A_rr^{-1} (B_r - A[r, <r] X_<r)), the update by one strided-batched
 // matrix-core GEMM and the diagonal solve by the small regime, both over all
 // problems; 2 * ceil(m/64) launches instead of a blocked solve per problem.
-// A single problem of that size takes this route too when it has at most
-// kRows64MaxRhs right-hand sides: with few columns the blocked path's
+// A single problem takes this route too when m <= kRows64SingleMaxM and it
+// has at most kRows64MaxRhs right-hand sides: there the blocked path's
 // inversion costs more than the substitution it replaces (measured on
-// MI355X, 1.1-3x for n <= 16 in all four types); with more columns the
-// inverse-times-block products of the blocked path win.
-constexpr int64_t kRows64MaxRhs = 32;
+// MI355X: 1.03-2.2x for n <= 16, m <= 192, in all four types); with more
+// columns or rows the inverse-times-block products of the blocked path win.
+constexpr int64_t kRows64MaxRhs = 16;
+constexpr int64_t kRows64SingleMaxM = 192;
 
 template <typename T>
 hipError_t medium_batched(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, int64_t strideA,
@@ -278,7 +279,8 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
     const bool small = path == HSMA_PATH_SMALL || (path == HSMA_PATH_AUTO && m <= 64);
     if (small) return hip_status(small_path<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
     if (path == HSMA_PATH_ROWS64 ||
-        (path == HSMA_PATH_AUTO && m <= kMediumMaxM && (batch > 1 || n <= kRows64MaxRhs)))
+        (path == HSMA_PATH_AUTO && m <= kMediumMaxM &&
+         (batch > 1 || (m <= kRows64SingleMaxM && n <= kRows64MaxRhs))))
         return hip_status(medium_batched<T>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, s));
 
     // Blocked path.

@@ -805,16 +805,15 @@ static bool blocked_inverse_applies(int64_t m, int nb)
 }
 
 // What HSMA_INV_AUTO takes: the blocked-inverse formula where it applies,
-// except for blocks of at most 256 in f64 and c64 (512 in c128), where one
-// column substitution launch measured faster on MI355X than the small
-// solves plus log2(nb / 64) rounds of merge products (whose fixed cost
-// dominates there).
+// except for blocks of 128 in f64 and c64 (of at most 256 in c128), where
+// one column substitution launch measured as fast or faster on MI355X than
+// the small solves plus log2(nb / 64) rounds of merge products.
 template <typename T>
 static bool auto_merges(int64_t m, int nb)
 {
     if (!blocked_inverse_applies<T>(m, nb)) return false;
     if (std::is_same<T, float>::value) return true;
-    return nb > (sizeof(T) == 16 ? 512 : 256);
+    return nb > (sizeof(T) == 16 ? 256 : 128);
 }
 
 template <typename T>

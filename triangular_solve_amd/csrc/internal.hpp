@@ -56,7 +56,7 @@ hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *in
 
 // Same, by route (HSMA_INV_*): AUTO takes the blocked-inverse formula (small
 // solver + batched GEMMs) when m is a multiple of nb and nb of 64 (nb >= 128;
-// nb > 256 for f64 and c64, nb > 512 for c128), else the column
+// nb > 128 for f64 and c64, nb > 256 for c128), else the column
 // substitution; FUSED inverts 2*ib
 // blocks in LDS and merges.
 // A route that does not apply to (m, nb, ib) gives hipErrorInvalidValue.
