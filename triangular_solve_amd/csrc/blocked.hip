@@ -250,7 +250,8 @@ template <> struct mfma_cfg<float, kTileWide> {
 };
 // FP32, small: a wave owns one 32 x 32 block, a 64 x 64 workgroup tile: four
 // times the workgroups of the standard tile for products that would leave
-// most CUs idle (the block-inverse merges, single problems in block rows).
+// CUs idle (the block-inverse merges, single problems in block rows, the
+// products of mid-size solves).
 template <> struct mfma_cfg<float, kTileSmall> {
     static constexpr int BLK = 32, LG = 2, NI = 1, NJ = 1, BK = 32;
     using acc_t = f32x16;
@@ -289,7 +290,7 @@ template <> struct vec16<float> { using type = f32x4; static constexpr int N = 4
 template <> struct vec16<double> { using type = f64x2; static constexpr int N = 2; };
 
 constexpr int kMaxBM = 256;    // largest workgroup tile height over the element types
-constexpr int64_t kSmallTileBelow = 256;  // standard-tile count under which the 64 x 64 tile runs
+constexpr int64_t kSmallTileBelow = 512;  // standard-tile count under which the 64 x 64 tile runs
 constexpr int kXcds = 8;        // XCDs of the GPU (round-robin workgroup placement)
 constexpr int64_t kGroupRows = 8;  // row tiles per group in the XCD-local tile order
 
@@ -619,8 +620,9 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     using CM = mfma_cfg<R, kTileSmall>;
     const bool wide = std::is_same<R, float>::value && !a_lower && p.Kr >= 2048 &&
                       ((p.Mr + CW::BM - 1) / CW::BM) * ((N + CW::BN - 1) / CW::BN) * batch >= 512;
-    // fewer standard tiles than CUs: the 64 x 64 tile (four times the
-    // workgroups of the same product)
+    // fewer than two standard tiles per CU: the 64 x 64 tile (four times the
+    // workgroups of the same product; measured on MI355X against a limit of
+    // one per CU, 1.0-1.27x faster solves, and mixed, 0.96-1.16x, at four)
     const bool small = !wide && ((p.Mr + CS::BM - 1) / CS::BM) * ((N + CS::BN - 1) / CS::BN) * batch <
                                     kSmallTileBelow;
     const int64_t kBM = wide ? CW::BM : small ? CM::BM : CS::BM;
