@@ -602,6 +602,7 @@ def main():
     st = bench_solve_tri(hs, torch)
     log("solve_tri 128 shape")
     st128 = bench_solve_tri(hs, torch, runs=1000, n=128, k=8, e2=4, e3=1)
+    st256 = bench_solve_tri(hs, torch, runs=1000, n=256, k=8, e2=4, e3=1)
     blocked = blocked16 = variants = inversion = few = None
     if not args.no_blocked:
         blocked = bench_blocked(hs, torch, 8192, DTYPES, runs=3)
@@ -624,7 +625,7 @@ def main():
                      "kernel": "colane_kernel (%s), %d algorithmic bytes per launch" % (dom, per[dom]["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "per_dtype": per,
-        "solve_tri": st, "solve_tri_128": st128,
+        "solve_tri": st, "solve_tri_128": st128, "solve_tri_256": st256,
         "blocked_8192": blocked,
         "blocked_16384": blocked16,
         "few_rhs_8192x64": few,

@@ -216,12 +216,11 @@ hsma_status hsma_trsm_strided_batched_general_z(int32_t side, int32_t uplo, int3
  *   X(i, c) = X[i*sX1 + c + i2*sX2 + i3*sX3]
  * Strides are in elements (floats), as the PR's reviewers asked. B is
  * read-only; X must not overlap A or B.
- * n <= 256 (any k). For n <= 128 one launch solves every batch entry on
- * chip (up to 64 rows one wave per group of right-hand sides, up to 128 rows
- * two waves that pass the finished rows through LDS), covering the
- * [128,128,4,1] case the PR's kernel reports as not supported; for
- * 128 < n <= 256 the rows are solved in blocks of 64, two launches per block
- * row, with the finished rows of X read back for the next block.
+ * n <= 256 (any k). One launch solves every batch entry on chip: up to 64
+ * rows one wave per group of right-hand sides; above that one wave per block
+ * of 64 rows (two, three or four), each block solved after the earlier ones
+ * have passed their finished rows through LDS -- covering the [128,128,4,1]
+ * case the PR's kernel reports as not supported.
  * n > 256 returns NOT_SUPPORTED.
  */
 hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float *B, float *X,

@@ -27,7 +27,8 @@ def test_every_kernel_reported_and_resident():
     res = resources()
     names = " ".join(res)
     for kernel in ("rowlane_kernel", "colane_kernel", "gemm_kernel", "diag_inv_kernel",
-                   "fused_inv_kernel", "tile_copy_kernel", "solve_tri_128_kernel", "reduce_kernel"):
+                   "fused_inv_kernel", "tile_copy_kernel", "solve_tri_128_kernel", "solve_tri_256_kernel",
+                   "reduce_kernel"):
         assert kernel in names, kernel
     for k, v in res.items():
         assert v.get("Occupancy", 0) >= 1, k

@@ -254,10 +254,11 @@ def test_repeat_runs_bitwise_identical(hs, dtype):
 
 
 def test_repeat_solve_tri_bitwise_identical(hs):
-    """The SOLVE_TRI kernels (one wave per group of right-hand sides, and the
-    two-wave 128-row kernel), 1000 runs each, bit for bit."""
+    """The SOLVE_TRI kernels (one wave per group of right-hand sides, the
+    two-wave 128-row kernel and the four-wave 256-row kernel), 1000 runs
+    each, bit for bit."""
     import torch
-    for n, k, e2, e3 in [(64, 6, 4, 2), (64, 10, 2, 2), (128, 8, 4, 1)]:
+    for n, k, e2, e3 in [(64, 6, 4, 2), (64, 10, 2, 2), (128, 8, 4, 1), (256, 8, 4, 1), (200, 40, 2, 1)]:
         A = synth.tri("f32", n, e2 * e3, seed=5, offdiag_div=n, layout="row")
         B = synth.rhs("f32", n, k, e2 * e3, seed=6, layout="row")
         dA, dB = to_dev(A), to_dev(B)

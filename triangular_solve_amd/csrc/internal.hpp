@@ -31,8 +31,8 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
                          int64_t strideA2, T *B, int64_t ldb, int64_t strideB, int64_t strideB2,
                          int64_t per, int64_t batch, hipStream_t s);
 
-// SOLVE_TRI (ggml row-major layout, f32) for 64 < n: block rows of 64, each
-// updated with the finished rows above and solved by small_rowlane in place.
+// SOLVE_TRI (ggml row-major layout, f32) for 64 < n <= 256: block rows of 64,
+// one wave each, in one launch (hipErrorInvalidValue outside that range).
 hipError_t solve_tri_medium(int64_t n, int64_t k, const float *A, const float *B, float *X,
                             int64_t ne02, int64_t ne03, int64_t sA1, int64_t sA2, int64_t sA3,
                             int64_t sB1, int64_t sB2, int64_t sB3, int64_t sX1, int64_t sX2,

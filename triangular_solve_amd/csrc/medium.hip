@@ -2,64 +2,18 @@
 //
 // llama.cpp PR #17457 ("SOLVE_TRI CUDA kernel for small matrices") keeps the
 // whole system in one thread block and reports n = 128 ([128,128,4,1]) as
-// not supported. Here the rows are cut into blocks of 64 and solved in
-// block-row order, the forward substitution applied blockwise:
+// not supported. Here the rows are cut into blocks of 64, one wave per block
+// row in one workgroup per (problem, group of right-hand sides), and solved
+// in block-row order, the forward substitution applied blockwise:
 //
 //   X_r = A_rr^{-1} (B_r - sum_{c < r} A_rc X_c),
 //
-// the update by update_kernel (lane = row, all finished rows above at once)
-// and the diagonal solve by the lane-per-row small-regime kernel, in place
-// on X, two launches per block row; for n <= 128 one launch does both block
-// rows (solve_tri_128_kernel).
+// one launch for any n <= 256 (solve_tri_128_kernel for two block rows,
+// solve_tri_256_kernel for three or four).
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace hsma {
-
-constexpr int kUpdCols = 8;  // right-hand-side columns per update workgroup
-
-// X[r0 + i][c] = B[r0 + i][c] - sum_{j < r0} A[r0 + i][j] X[j][c] for the rows
-// i < rows of the block row starting at r0 and columns c of this workgroup.
-// One wave per (problem, group of kUpdCols columns); row-major ggml strides in
-// elements (row stride s*1, batch strides s*2, s*3).
-__global__ void __launch_bounds__(64) update_kernel(const float *__restrict__ A, int64_t sA1,
-                                                    int64_t sA2, int64_t sA3,
-                                                    const float *__restrict__ B, int64_t sB1,
-                                                    int64_t sB2, int64_t sB3, float *X,
-                                                    int64_t sX1, int64_t sX2, int64_t sX3,
-                                                    int r0, int rows, int64_t k, int64_t ne02)
-{
-    const int64_t b = blockIdx.x;
-    const int64_t i2 = b % ne02, i3 = b / ne02;
-    const int lane = threadIdx.x;
-    const bool live = lane < rows;
-    const int64_t i = r0 + (live ? lane : 0);
-    const int64_t c0 = (int64_t)blockIdx.y * kUpdCols;
-    const float *Ar = A + i2 * sA2 + i3 * sA3 + i * sA1;
-    const float *Bb = B + i2 * sB2 + i3 * sB3;
-    float *Xb = X + i2 * sX2 + i3 * sX3;
-
-    float acc[kUpdCols];
-#pragma unroll
-    for (int c = 0; c < kUpdCols; ++c) {
-        const int64_t cc = c0 + c < k ? c0 + c : k - 1;  // columns past k repeat a valid one
-        acc[c] = Bb[i * sB1 + cc];
-    }
-    for (int j = 0; j < r0; ++j) {
-        const float a = Ar[j];
-        const float *xr = Xb + (int64_t)j * sX1;
-#pragma unroll
-        for (int c = 0; c < kUpdCols; ++c) {
-            const int64_t cc = c0 + c < k ? c0 + c : k - 1;
-            acc[c] = __builtin_fmaf(-a, xr[cc], acc[c]);
-        }
-    }
-    if (live) {
-#pragma unroll
-        for (int c = 0; c < kUpdCols; ++c)
-            if (c0 + c < k) Xb[i * sX1 + c0 + c] = acc[c];
-    }
-}
 
 // Forward substitution of one wave's 64 rows (lane = row), coefficients
 // a[j] = a_ij / a_ii below the diagonal and 0 elsewhere, w = b / a_ii. Step j
@@ -193,43 +147,129 @@ static hipError_t launch_128(bool vec, int64_t n, int64_t k, const float *A, con
     return hipGetLastError();
 }
 
+// 128 < n <= 256 in one launch: four waves per (problem, group of KW
+// columns), lane = row, wave w owning rows 64w .. 64w+63. At stage s wave s
+// solves its diagonal block (its rows already hold B_s - sum_{c<s} A_sc X_c)
+// and publishes X_s in LDS; after the barrier every later wave subtracts
+// A_ws X_s, reading its row's 64 coefficients of block s from memory (16-byte
+// loads when VEC) and X_s as LDS broadcasts. Coefficients of the diagonal
+// block are scaled by the row's 1/a_ii, as in the small regime.
+template <int KW, bool VEC>
+__global__ void __launch_bounds__(256) solve_tri_256_kernel(
+    const float *__restrict__ A, int64_t sA1, int64_t sA2, int64_t sA3, const float *__restrict__ B,
+    int64_t sB1, int64_t sB2, int64_t sB3, float *__restrict__ X, int64_t sX1, int64_t sX2,
+    int64_t sX3, int n, int64_t k, int64_t ne02)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __shared__ float xs[256 * KW];
+    const int64_t b = blockIdx.x;
+    const int64_t i2 = b % ne02, i3 = b / ne02;
+    const int64_t c0 = (int64_t)blockIdx.y * KW;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int i = wave * 64 + lane;          // row of this lane
+    const bool live = i < n;
+    const int nblk = (n + 63) / 64;          // 3 or 4, the same for every wave
+    const float *Ar = A + i2 * sA2 + i3 * sA3 + (int64_t)(live ? i : 0) * sA1;
+    const float *Bb = B + i2 * sB2 + i3 * sB3;
+    float *Xb = X + i2 * sX2 + i3 * sX3;
+
+    // the row's coefficients in columns 64c .. 64c+63 (0 past n)
+    auto load_block = [&](int c, float (&v)[64]) {
+        const int base = 64 * c;
+#pragma unroll
+        for (int t = 0; t < 64; t += 4) {
+            if (VEC && base + t + 4 <= n) {
+                const f4 x = *(const f4 *)(Ar + base + t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[t + e] = x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[t + e] = base + t + e < n ? Ar[base + t + e] : 0.0f;
+            }
+        }
+    };
+
+    const float inv = live ? 1.0f / Ar[i] : 1.0f;
+    float w[KW];
+#pragma unroll
+    for (int q = 0; q < KW; ++q)
+        w[q] = (live && c0 + q < k) ? Bb[(int64_t)i * sB1 + c0 + q] : 0.0f;
+    float a[64];
+    if (wave < nblk) {
+        float v[64];
+        load_block(wave, v);
+#pragma unroll
+        for (int j = 0; j < 64; ++j) a[j] = (live && j < lane) ? v[j] * inv : 0.0f;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) a[j] = 0.0f;
+    }
+
+    for (int s = 0; s < nblk; ++s) {
+        if (wave == s) {
+#pragma unroll
+            for (int q = 0; q < KW; ++q) w[q] *= inv;
+            wave_substitute<KW>(a, w);
+#pragma unroll
+            for (int q = 0; q < KW; ++q) xs[(64 * s + lane) * KW + q] = w[q];
+        }
+        __syncthreads();
+        if (wave > s && wave < nblk) {
+            float v[64];
+            load_block(s, v);
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                const float aij = live ? v[j] : 0.0f;
+#pragma unroll
+                for (int q = 0; q < KW; ++q)
+                    w[q] = __builtin_fmaf(-aij, xs[(64 * s + j) * KW + q], w[q]);
+            }
+        }
+    }
+    if (live) {
+#pragma unroll
+        for (int q = 0; q < KW; ++q)
+            if (c0 + q < k) Xb[(int64_t)i * sX1 + c0 + q] = w[q];
+    }
+}
+
+template <int KW>
+static hipError_t launch_256(bool vec, int64_t n, int64_t k, const float *A, const float *B,
+                             float *X, int64_t nprob, int64_t ne02, int64_t sA1, int64_t sA2,
+                             int64_t sA3, int64_t sB1, int64_t sB2, int64_t sB3, int64_t sX1,
+                             int64_t sX2, int64_t sX3, hipStream_t s)
+{
+    const int64_t chunks = (k + KW - 1) / KW;
+    if (chunks > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)nprob, (unsigned)chunks);
+    if (vec)
+        hipLaunchKernelGGL((solve_tri_256_kernel<KW, true>), grid, dim3(256), 0, s, A, sA1, sA2, sA3,
+                           B, sB1, sB2, sB3, X, sX1, sX2, sX3, (int)n, k, ne02);
+    else
+        hipLaunchKernelGGL((solve_tri_256_kernel<KW, false>), grid, dim3(256), 0, s, A, sA1, sA2,
+                           sA3, B, sB1, sB2, sB3, X, sX1, sX2, sX3, (int)n, k, ne02);
+    return hipGetLastError();
+}
+
 hipError_t solve_tri_medium(int64_t n, int64_t k, const float *A, const float *B, float *X,
                             int64_t ne02, int64_t ne03, int64_t sA1, int64_t sA2, int64_t sA3,
                             int64_t sB1, int64_t sB2, int64_t sB3, int64_t sX1, int64_t sX2,
                             int64_t sX3, hipStream_t s)
 {
     const int64_t nprob = ne02 * ne03;
-    const int64_t ychunks = (k + kUpdCols - 1) / kUpdCols;
-    if (nprob > 0x7fffffff || ychunks > 65535) return hipErrorInvalidConfiguration;
+    if (nprob > 0x7fffffff || n <= 64 || n > 256) return hipErrorInvalidValue;
+    // fewer columns per workgroup shorten each wave's dependent chain; more
+    // share the row loads of A
+    const bool vec = (uintptr_t)A % 16 == 0 && (sA1 * 4) % 16 == 0 && (sA2 * 4) % 16 == 0 &&
+                     (sA3 * 4) % 16 == 0;
     if (n <= 128) {
-        // fewer columns per workgroup shorten each wave's dependent chain;
-        // more share the row loads of A
-        const bool vec = (uintptr_t)A % 16 == 0 && (sA1 * 4) % 16 == 0 && (sA2 * 4) % 16 == 0 &&
-                         (sA3 * 4) % 16 == 0;
         if (k <= 8) return launch_128<2>(vec, n, k, A, B, X, nprob, ne02, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3, s);
         if (k <= 32) return launch_128<4>(vec, n, k, A, B, X, nprob, ne02, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3, s);
         return launch_128<8>(vec, n, k, A, B, X, nprob, ne02, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3, s);
     }
-    for (int64_t r0 = 0; r0 < n; r0 += 64) {
-        const int64_t rows = n - r0 < 64 ? n - r0 : 64;
-        const float *Brow = B + r0 * sB1;
-        int64_t sb1 = sB1, sb2 = sB2, sb3 = sB3;
-        if (r0 > 0) {
-            hipLaunchKernelGGL(update_kernel, dim3((unsigned)nprob, (unsigned)ychunks), dim3(64), 0, s,
-                               A, sA1, sA2, sA3, B, sB1, sB2, sB3, X, sX1, sX2, sX3, (int)r0,
-                               (int)rows, k, ne02);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            // the diagonal solve then runs in place on the updated rows of X
-            Brow = X + r0 * sX1;
-            sb1 = sX1; sb2 = sX2; sb3 = sX3;
-        }
-        hipError_t e = small_rowlane<float>(A + r0 * sA1 + r0, sA1, 1, sA2, sA3, Brow, sb1, 1, sb2,
-                                            sb3, X + r0 * sX1, sX1, 1, sX2, sX3, rows, k, ne02,
-                                            ne03, 1.0f, s);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    if (k <= 8) return launch_256<2>(vec, n, k, A, B, X, nprob, ne02, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3, s);
+    if (k <= 32) return launch_256<4>(vec, n, k, A, B, X, nprob, ne02, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3, s);
+    return launch_256<8>(vec, n, k, A, B, X, nprob, ne02, sA1, sA2, sA3, sB1, sB2, sB3, sX1, sX2, sX3, s);
 }
 
 }  // namespace hsma
