@@ -620,11 +620,14 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     using CM = mfma_cfg<R, kTileSmall>;
     const bool wide = std::is_same<R, float>::value && !a_lower && p.Kr >= 2048 &&
                       ((p.Mr + CW::BM - 1) / CW::BM) * ((N + CW::BN - 1) / CW::BN) * batch >= 512;
-    // fewer than two standard tiles per CU: the 64 x 64 tile (four times the
-    // workgroups of the same product; measured on MI355X against a limit of
-    // one per CU, 1.0-1.27x faster solves, and mixed, 0.96-1.16x, at four)
-    const bool small = !wide && ((p.Mr + CS::BM - 1) / CS::BM) * ((N + CS::BN - 1) / CS::BN) * batch <
-                                    kSmallTileBelow;
+    // the 64 x 64 tile: for fewer than two standard tiles per CU (four times
+    // the workgroups of the same product; measured on MI355X against a limit
+    // of one per CU, 1.0-1.27x faster solves, and mixed, 0.96-1.16x, at
+    // four), and for products whose rows or columns fit one small tile (a
+    // standard tile would be at least half padding)
+    const bool small = !wide && (((p.Mr + CS::BM - 1) / CS::BM) * ((N + CS::BN - 1) / CS::BN) * batch <
+                                     kSmallTileBelow ||
+                                 p.Mr <= CM::BM || N <= CM::BN);
     const int64_t kBM = wide ? CW::BM : small ? CM::BM : CS::BM;
     const int64_t kBN = wide ? CW::BN : small ? CM::BN : CS::BN;
     const int64_t gx = (p.Mr + kBM - 1) / kBM;
