@@ -35,3 +35,17 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
                         "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_repeats_to_its_time_budget():
+    """The CPU baseline times the oracle on the step's problems, repeated until
+    its time budget is spent, and reports the repeats and thread count."""
+    import synth
+    host = {dt: bench.batched_inputs(dt, 64, 64, 8, seed=7) for dt in bench.DTYPES}
+    out = bench.cpu_baseline(host, min_seconds=0.2)
+    assert out["kind"] == "oracle" and out["unit"] == "GFLOPS"
+    assert out["seconds"] >= 0.2 and out["repeats"] >= 1 and out["cores"] >= 1
+    flops = sum(bench.lapack_flops(dt, 64, 64) * 8 for dt in bench.DTYPES) * out["repeats"]
+    assert abs(out["value"] - flops / out["seconds"] / 1e9) <= 1e-9 * out["value"]
+    assert "%d times" % out["repeats"] in out["sample"]
+    del synth
