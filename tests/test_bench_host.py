@@ -40,7 +40,6 @@ def test_multi_gpu_refused():
 def test_cpu_baseline_repeats_to_its_time_budget():
     """The CPU baseline times the oracle on the step's problems, repeated until
     its time budget is spent, and reports the repeats and thread count."""
-    import synth
     host = {dt: bench.batched_inputs(dt, 64, 64, 8, seed=7) for dt in bench.DTYPES}
     out = bench.cpu_baseline(host, min_seconds=0.2)
     assert out["kind"] == "oracle" and out["unit"] == "GFLOPS"
@@ -48,4 +47,3 @@ def test_cpu_baseline_repeats_to_its_time_budget():
     flops = sum(bench.lapack_flops(dt, 64, 64) * 8 for dt in bench.DTYPES) * out["repeats"]
     assert abs(out["value"] - flops / out["seconds"] / 1e9) <= 1e-9 * out["value"]
     assert "%d times" % out["repeats"] in out["sample"]
-    del synth
