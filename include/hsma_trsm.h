@@ -106,11 +106,11 @@ hsma_status hsma_trsm_z(int64_t m, int64_t n, hsma_double_complex alpha,
  * strideA == 0 shares one A across the batch. B blocks must not overlap:
  * strideB >= ldb*n when batch_count > 1 (else INVALID_SIZE).
  * m <= 64 runs as one launch over the whole batch (the pages' small regime);
- * 64 < m <= 256 runs in block rows of 64 over the whole batch (per block row
+ * 64 < m <= 512 runs in block rows of 64 over the whole batch (per block row
  * one batched GEMM update with the finished rows and one batched small-regime
  * solve of the diagonal blocks); larger m runs the blocked solver once per
  * problem.
- * Errors: as hsma_trsm_*; ALLOC_FAILED only for m > 256.
+ * Errors: as hsma_trsm_*; ALLOC_FAILED only for m > 512.
  */
 hsma_status hsma_trsm_strided_batched_s(int64_t m, int64_t n, float alpha, const float *A,
                                         int64_t lda, int64_t strideA, float *B, int64_t ldb,
@@ -247,10 +247,10 @@ hsma_status hsma_solve_tri_f32(int64_t n, int64_t k, const float *A, const float
  *         route always starts from 64 x 64 sub-blocks (the small-regime
  *         solver's size) and ignores ib.
  *   path  HSMA_PATH_AUTO, HSMA_PATH_SMALL (requires m <= 64),
- *         HSMA_PATH_BLOCKED (any m >= 1) or HSMA_PATH_ROWS64 (m <= 256:
+ *         HSMA_PATH_BLOCKED (any m >= 1) or HSMA_PATH_ROWS64 (m <= 512:
  *         block rows of 64, each updated by one matrix-core GEMM with the
  *         finished rows and solved by the small regime, no inversion and no
- *         workspace; what AUTO takes for batches with 64 < m <= 256
+ *         workspace; what AUTO takes for batches with 64 < m <= 512
  *         and for single problems with 64 < m <= 192 and n <= 16)
  *   inv   route of the diagonal-block inversion (blocked path):
  *         HSMA_INV_AUTO: BLOCKED where it applies (for f64 and c64 only

@@ -68,7 +68,7 @@ def test_ex_option_checks(hs):
     f = hs.entry("ex", "f64")
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"path": 7}, 0) == hs.INVALID_VALUE
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"path": hs.PATH_SMALL}, 0) == hs.INVALID_VALUE
-    assert f(257, 4, 1, BAD, 257, BAD, 257, {"path": hs.PATH_ROWS64}, 0) == hs.INVALID_VALUE
+    assert f(513, 4, 1, BAD, 513, BAD, 513, {"path": hs.PATH_ROWS64}, 0) == hs.INVALID_VALUE
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"path": 4}, 0) == hs.INVALID_VALUE
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 100}, 0) == hs.INVALID_VALUE   # not a multiple of 16
     assert f(100, 4, 1, BAD, 100, BAD, 100, {"nb": 2048}, 0) == hs.INVALID_VALUE
@@ -164,7 +164,7 @@ def test_alloc_failure_injection(hs, t, monkeypatch):
     assert hs.entry("trsm", t)(300, 8, 1, BAD, 300, BAD, 300, 0) == hs.ALLOC_FAILED
     assert hs.entry("ex", t)(300, 8, 1, BAD, 300, BAD, 300, {"nb": 128, "path": hs.PATH_BLOCKED},
                              0) == hs.ALLOC_FAILED
-    assert hs.entry("strided_batched", t)(300, 8, 1, BAD, 300, 0, BAD, 300, 2400, 3, 0) == hs.ALLOC_FAILED
+    assert hs.entry("strided_batched", t)(600, 8, 1, BAD, 600, 0, BAD, 600, 4800, 3, 0) == hs.ALLOC_FAILED
     assert hs.entry("diag_inv_ex", t)(1024, {"nb": 512, "inv": hs.INV_BLOCKED}, BAD, 1024, BAD,
                                       0) == hs.ALLOC_FAILED
     assert hs.hsma_status_string(hs.ALLOC_FAILED) == "workspace allocation failed"

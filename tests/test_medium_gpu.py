@@ -33,7 +33,8 @@ def batched(hs, dtype, m, n, batch, alpha=1.0, lda=None, ldb=None, shared_a=Fals
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("m,n,batch", [(65, 1, 3), (100, 7, 5), (128, 64, 6), (200, 100, 2),
-                                       (256, 33, 4), (192, 64, 50)])
+                                       (256, 33, 4), (192, 64, 50), (300, 20, 3), (512, 64, 4),
+                                       (457, 129, 2)])
 def test_medium_batched(hs, dtype, m, n, batch):
     say("medium batched", dtype, m, n, batch)
     A, B, X = batched(hs, dtype, m, n, batch, seed=m + n + batch)

@@ -75,9 +75,11 @@ def test_variants_small(hs, dt, side, uplo, trans, diag):
 @pytest.mark.parametrize("side,uplo,trans,diag", VARIANTS)
 def test_variants_medium_batched(hs, dt, side, uplo, trans, diag):
     say("variant medium batched", dt, side, uplo, trans, diag)
-    m, n = (130, 70) if side == "L" else (70, 130)
-    Xg, Xo = run_variant(hs, dt, side, uplo, trans, diag, m, n, 5, 1.0, seed=7, pad=(2, 3))
-    assert rel_err(Xg, Xo) <= TOL_LARGE[dt]
+    for m, n, batch in ((130, 70, 5), (390, 40, 3)):
+        if side != "L":
+            m, n = n, m
+        Xg, Xo = run_variant(hs, dt, side, uplo, trans, diag, m, n, batch, 1.0, seed=7, pad=(2, 3))
+        assert rel_err(Xg, Xo) <= TOL_LARGE[dt], (m, n, batch)
 
 
 @pytest.mark.parametrize("dt", DTYPES)
