@@ -29,6 +29,11 @@
  *     once per device and keeps until the process ends; freed workspace stays
  *     in that pool for the next call (its size is at most the largest
  *     workspace used so far) instead of being returned to the driver.
+ *   - The blocked path also runs some copies on a second stream the library
+ *     creates once per device (non-blocking, default priority, kept until
+ *     the process ends), ordered against `stream` with events: `stream`
+ *     waits for them before the call's work on it ends, so a call remains
+ *     one ordered piece of work on `stream` (also under graph capture).
  *   - No singularity check: a zero or NaN diagonal entry produces inf/NaN
  *     under IEEE rules (the SOLVE_TRI review in llama.cpp PR #17457 dropped
  *     its zero-pivot guard for the same reason). Pivots are applied as
