@@ -33,7 +33,7 @@
  *     creates once per device (non-blocking, default priority, kept until
  *     the process ends), ordered against `stream` with events: `stream`
  *     waits for them before the call's work on it ends, so a call remains
- *     one ordered piece of work on `stream` (also under graph capture).
+ *     one ordered piece of work on `stream`.
  *   - No singularity check: a zero or NaN diagonal entry produces inf/NaN
  *     under IEEE rules (the SOLVE_TRI review in llama.cpp PR #17457 dropped
  *     its zero-pivot guard for the same reason). Pivots are applied as
