@@ -56,6 +56,8 @@ ZERO_CASES = [  # (m, n, batch, route, zero pivot row)
     (64, 64, 4, "batched", 0), (64, 64, 4, "batched", 37), (64, 64, 4, "batched", 63),
     (64, 6, 4, "batched", 20), (37, 64, 2, "batched", 30),
     (150, 64, 3, "batched", 100),                 # block rows of 64 over the batch
+    (400, 30, 2, "batched", 350),                 # the same up to m = 512
+    (150, 8, 1, "batched", 120),                  # one problem with few columns: block rows
     (300, 40, 1, "blocked:128", 5), (300, 40, 1, "blocked:128", 200),   # column route
     (512, 40, 1, "blocked:256", 70), (512, 40, 1, "blocked:256", 300),  # blocked-inverse route
 ]
@@ -77,7 +79,8 @@ def test_zero_pivot_matches_oracle(hs, dt, m, n, batch, route, k):
     assert np.isfinite(Xo[:, :k, :]).all() and not np.isfinite(Xo[:, k:, :]).any()
 
 
-@pytest.mark.parametrize("n,k", [(64, 10), (16, 10), (200, 100), (128, 127), (100, 3)])
+@pytest.mark.parametrize("n,k", [(64, 10), (16, 10), (200, 100), (128, 127), (100, 3), (256, 230),
+                                 (150, 140), (193, 64)])
 def test_zero_pivot_solve_tri(hs, n, k):
     import torch
     say("zero pivot solve_tri", n, k)
