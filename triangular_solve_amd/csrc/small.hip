@@ -313,6 +313,23 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// B and X stream through the vector path with the non-temporal hint: each
+// line is used once, and marking it for early eviction leaves L2 to the
+// triangle lines that the coefficient prefetch brings in ahead of the scalar
+// loads (4096 problems of 64 x 64, MI355X: f32 51.6 -> 38.8 us, f64
+// 97.8 -> 83.6 us, c64 127 -> 114 us per launch).
+template <typename T>
+__device__ __forceinline__ v4i ld_b(gptr<T> p)
+{
+    return __builtin_nontemporal_load((const gptr<v4i>)p);
+}
+template <bool NT = true, typename T>
+__device__ __forceinline__ void st_x(gptr<T> p, v4i v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, (gptr<v4i>)p);
+    else *(gptr<v4i>)p = v;
+}
+
 // Per-wave LDS tile of 64 columns x one 128-byte line; the 16-byte pad of
 // the column stride keeps both the line-wise and the column-wise 16-byte
 // accesses free of bank conflicts.
@@ -470,10 +487,42 @@ struct TouchPlan {
     static constexpr Table T = build();
 };
 
+// Kept-column panels (f64, c64): the whole 64-row column stays in registers
+// and is solved in row panels of one 128-byte line; a panel applies the
+// finished rows of the earlier panels straight from registers (no row is read
+// back from memory, and each element sees its updates in the same order as
+// in one panel), while the next panel's lines of B are on their way. f32
+// solves its kept column in one panel; double complex keeps only its current
+// panel (a whole column would take all 256 VGPRs) and reads the earlier rows
+// back from X.
+template <typename T>
+constexpr bool kKeep = sizeof(T) == 8;
+
+// Row panels per 64-row column.
+template <typename T>
+constexpr int kPanels = kKeep<T> ? 64 * (int)sizeof(T) / 128 : sizeof(T) == 16 ? 2 : 1;
+
+// Where the coefficient prefetch loads land. Their results are never used;
+// a load into registers has to be waited for before the registers are
+// reused (and the wait, in issue order, also waits for every load issued
+// before it, such as the next panel's B lines), so the kept-column panels
+// direct them into a few LDS bytes that nothing reads.
+// For the single-panel f32 solve the waits are harmless and the LDS form
+// measured slower (38.4 -> 47.5 us per 4096 problems).
+template <typename T>
+constexpr bool kTouchLds = kKeep<T>;
+
+// Registers of a lane's column, and the register of panel row 0 of the panel
+// at rows R0.
+template <typename T, int P>
+constexpr int kRegs = kKeep<T> ? 64 : P;
+template <typename T, int R0>
+constexpr int kRegOff = kKeep<T> ? R0 : 0;
+
 // Per-panel state shared by the batch recursion below.
 template <typename T, int P>
 struct PanelState {
-    T w[P];       // this lane's rows of the panel
+    T w[kRegs<T, P>];  // this lane's rows (all of them, or the current panel's)
     T x;          // multiplier of the current column segment
     cptr<T> a4;   // A of this problem (scalar loads)
     int64_t lda;
@@ -483,6 +532,7 @@ struct PanelState {
     lptr tile;    // this wave's LDS tile
     int lane128;  // lane * 128: this lane's line of a prefetched segment
     int tv[64];   // results of the segments' prefetch loads, retired later
+    lptr sink;    // LDS bytes the prefetch loads write to (never read)
     T myinv;      // 1/a_ll of this lane's row index l
 };
 
@@ -510,12 +560,12 @@ __device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int
     }
     v4i cur[8], nxt[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cur[q] = *(const gptr<v4i>)(bw + goff[q]);
+    for (int q = 0; q < 8; ++q) cur[q] = ld_b(bw + goff[q]);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
         if (ch + 1 < NCH) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) nxt[q] = *(const gptr<v4i>)(bw + goff[q] + (ch + 1) * L);
+            for (int q = 0; q < 8; ++q) nxt[q] = ld_b(bw + goff[q] + (ch + 1) * L);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q)
@@ -546,7 +596,7 @@ __device__ __forceinline__ void load_panel(PanelState<T, P> &st, gptr<T> bw, int
 
 // st.w into rows [r0, r0 + P) of the wave's columns, the reverse of
 // load_panel (columns past ncol are not written).
-template <typename T, int P>
+template <typename T, int P, bool NT = true>
 __device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, int r0)
 {
     constexpr int V = 16 / (int)sizeof(T);
@@ -570,7 +620,7 @@ __device__ __forceinline__ void store_panel(PanelState<T, P> &st, gptr<T> bw, in
         for (int q = 0; q < 8; ++q) {
             const int col = q * 8 + (lane >> 3);
             const v4i v = *(const lptr_v4i)(st.tile + col * kTileCol + sub * 16);
-            if (col < st.ncol) *(gptr<v4i>)(bw + col * st.ldb + r0 + ch * L + sub * V) = v;
+            if (col < st.ncol) st_x<NT>(bw + col * st.ldb + r0 + ch * L + sub * V, v);
         }
         wave_lds_sync();
     }
@@ -642,15 +692,19 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
         using Plan = PanelPlan<P, R0, G, kDiagInStream<T>>;
         constexpr auto pc = Plan::T.pc[Q];
         constexpr int off = Plan::T.off[Q];
+        constexpr int wo = kRegOff<T, R0>;
         if constexpr (pc.first) {
-            if constexpr (pc.reload) {
+            if constexpr (pc.reload && kKeep<T>) {
+                // finished x_k of an earlier panel, still in its register
+                st.x = st.w[pc.col];
+            } else if constexpr (pc.reload) {
                 // finished x_k of an earlier panel, read back from B through
                 // the tile: one line of rows per refill for all the wave's
                 // columns, then one LDS read per segment
                 if constexpr (pc.col % 8 == 0) reload_fill<T, P>(st, pc.col);
                 st.x = reload_x<T, P>(st, pc.col % 8);
             } else if constexpr (pc.diag) {
-                constexpr int j = pc.col - R0;
+                constexpr int j = wo + pc.col - R0;
                 if constexpr (std::is_same<T, float>::value) {
                     float r = __builtin_amdgcn_rcpf(cb[off]);
                     asm volatile("" : "+v"(r) : "v"(st.w[j]));
@@ -671,7 +725,7 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
                 }
                 st.w[j] = st.x;
             } else {
-                constexpr int j = pc.col - R0;
+                constexpr int j = wo + pc.col - R0;
                 // Tie the broadcast of 1/a_jj to w[j] so the compiler cannot
                 // hoist all broadcasts to the top (that would exhaust SGPRs).
                 T inv = st.myinv;
@@ -685,7 +739,8 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
             }
         }
 #pragma unroll
-        for (int r = pc.lo + pc.diag; r < pc.hi; ++r) st.w[r] = fms(st.w[r], cb[off + r - pc.lo], st.x);
+        for (int r = pc.lo + pc.diag; r < pc.hi; ++r)
+            st.w[wo + r] = fms(st.w[wo + r], cb[off + r - pc.lo], st.x);
         batch_compute<T, P, R0, G, Q + 1, Q1>(st, cb);
     }
 }
@@ -704,7 +759,11 @@ __device__ __forceinline__ void batch_touch(PanelState<T, P> &st, cptr<T> ap)
         const int bytes = (int)(first - line) + (sg.hi - sg.lo) * (int)sizeof(T);
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void *)line, (short)0, bytes, 0x00020000);
-        st.tv[S] = __builtin_amdgcn_raw_buffer_load_b32(rs, st.lane128, 0, 0);
+        if constexpr (kTouchLds<T>)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)st.sink, 4,
+                                                     st.lane128, 0, 0, 0);
+        else
+            st.tv[S] = __builtin_amdgcn_raw_buffer_load_b32(rs, st.lane128, 0, 0);
         batch_touch<T, P, R0, G, AH, S + 1, S1>(st, ap);
     }
 }
@@ -734,7 +793,7 @@ __device__ __forceinline__ void run_batches(PanelState<T, P> &st)
         batch_touch<T, P, R0, G, AH, TP::T.tfirst[Bi], TP::T.tfirst[Bi + 1]>(st, ap);
         T cb[G];
         batch_load<T, P, R0, G, p0, p1>(cb, ap, st.lda);
-        batch_retire<T, P, TP::T.cfirst[Bi], TP::T.cfirst[Bi + 1]>(st);
+        if constexpr (!kTouchLds<T>) batch_retire<T, P, TP::T.cfirst[Bi], TP::T.cfirst[Bi + 1]>(st);
         batch_compute<T, P, R0, G, p0, p1>(st, cb);
         __builtin_amdgcn_sched_barrier(0);
         run_batches<T, P, R0, G, AH, Bi + 1>(st);
@@ -752,10 +811,109 @@ __device__ __forceinline__ void run_panels(PanelState<T, P> &st, T alpha, bool s
         load_panel<T, P>(st, bw, r0, alpha, scale);
         st.x = zero_of(T());
         run_batches<T, P, r0, kBatch<T>, kAhead<T>, 0>(st);
-        store_panel<T, P>(st, bw, r0);
+        // the rows of an earlier panel are read back moments later: those
+        // stores go through L2 normally (c128, 4096 problems: 205 -> 195 us)
+        store_panel<T, P, (PI + 1 == NPANEL)>(st, bw, r0);
         typename traits<T>::real wl;
         if constexpr (traits<T>::is_complex) wl = st.w[P - 1].re; else wl = st.w[P - 1];
         run_panels<T, P, NPANEL, PI + 1>(st, alpha, scale, wl);
+    }
+}
+
+// Kept-column panels: the loads of the rows [r0, r0 + P) of the wave's
+// columns (one 128-byte line per column), 8 lanes per line.
+template <typename T, int P>
+__device__ __forceinline__ void panel_issue(const PanelState<T, P> &st, gptr<T> bw, int r0, v4i (&nb)[8])
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    static_assert(P * (int)sizeof(T) == 128, "a kept-column panel is one line per column");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        int col = q * 8 + (lane >> 3);
+        col = col < st.ncol ? col : st.ncol - 1;  // duplicates of a valid column
+        nb[q] = ld_b(bw + (col * st.ldb + r0 + (lane & 7) * V));
+    }
+}
+
+// alpha * the loaded rows into registers [R0, R0 + P) of the column, lane =
+// column, through the wave's tile.
+template <typename T, int P, int R0>
+__device__ __forceinline__ void panel_finish(PanelState<T, P> &st, const v4i (&nb)[8], T alpha, bool scale)
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        *(lptr_v4i)(st.tile + (q * 8 + (lane >> 3)) * kTileCol + sub * 16) = nb[q];
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const v4i v = *(const lptr_v4i)(st.tile + lane * kTileCol + k * 16);
+        T t[V];
+        __builtin_memcpy(t, &v, 16);
+#pragma unroll
+        for (int e = 0; e < V; ++e) st.w[R0 + k * V + e] = t[e];
+    }
+    wave_lds_sync();
+    if (scale) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) st.w[R0 + e] = mul(alpha, st.w[R0 + e]);
+    }
+}
+
+// Registers [R0, R0 + P) into rows [R0, R0 + P) of the wave's columns.
+template <typename T, int P, int R0>
+__device__ __forceinline__ void panel_store(PanelState<T, P> &st, gptr<T> bw)
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 7;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        T t[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) t[e] = st.w[R0 + k * V + e];
+        v4i v;
+        __builtin_memcpy(&v, t, 16);
+        *(lptr_v4i)(st.tile + lane * kTileCol + k * 16) = v;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int col = q * 8 + (lane >> 3);
+        const v4i v = *(const lptr_v4i)(st.tile + col * kTileCol + sub * 16);
+        if (col < st.ncol) st_x(bw + col * st.ldb + R0 + sub * V, v);
+    }
+    wave_lds_sync();
+}
+
+// Panel PI of a kept column: its B lines (nb) were requested during the
+// previous panel; request the next panel's, solve this one, store its rows of
+// X (the stores drain while the next panel is solved). The coefficient
+// prefetch runs ahead of the stream as in the single-panel solve, into the
+// LDS sink, so that nothing waits for it.
+template <typename T, int P, int NPANEL, int PI>
+__device__ __forceinline__ void run_panels_keep(PanelState<T, P> &st, const T *Ap, gptr<T> bw, T alpha,
+                                                bool scale, v4i (&nb)[8])
+{
+    if constexpr (PI < NPANEL) {
+        constexpr int r0 = PI * P;
+        if constexpr (!kDiagInStream<T>) {
+            // 1/a_ll for the panel's rows l (lane l mod P holds row l)
+            const int l = r0 + ((threadIdx.x & 63) & (P - 1));
+            st.myinv = recip(ld_global<T>((gptr<T>)(uint64_t)(Ap + (l + l * st.lda)), 0));
+        }
+        panel_finish<T, P, r0>(st, nb, alpha, scale);
+        if constexpr (PI + 1 < NPANEL) panel_issue<T, P>(st, bw, r0 + P, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        st.x = zero_of(T());
+        run_batches<T, P, r0, kBatch<T>, kAhead<T>, 0>(st);
+        // no prefetch may still be writing the LDS sink when the wave ends
+        if constexpr (PI + 1 == NPANEL) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        panel_store<T, P, r0>(st, bw);
+        run_panels_keep<T, P, NPANEL, PI + 1>(st, Ap, bw, alpha, scale, nb);
     }
 }
 
@@ -768,6 +926,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
                                                          int64_t strideB2)
 {
     extern __shared__ __attribute__((aligned(16))) char colane_lds[];
+    __shared__ int colane_sink[64];
     constexpr int M = 64;
     constexpr int P = M / NPANEL;
     const int lane = threadIdx.x & 63;
@@ -793,10 +952,19 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     st.ldb = ldb;
     st.ncol = (int)(n - cfirst < 64 ? n - cfirst : 64);
     st.tile = (lptr)colane_lds + wave * kTileBytes;
+    st.sink = (lptr)colane_sink;
 
     st.lane128 = lane * 128;
-    if constexpr (!kDiagInStream<T>) st.myinv = recip(Ap[lane + lane * lda]);
-    run_panels<T, P, NPANEL, 0>(st, alpha, scale != 0, typename traits<T>::real(0));
+    if constexpr (kKeep<T> && NPANEL > 1) {
+        const gptr<T> bw = (gptr<T>)(uint64_t)Bc0;
+        v4i nb[8];
+        panel_issue<T, P>(st, bw, 0, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        run_panels_keep<T, P, NPANEL, 0>(st, Ap, bw, alpha, scale != 0, nb);
+    } else {
+        if constexpr (!kDiagInStream<T>) st.myinv = recip(Ap[lane + lane * lda]);
+        run_panels<T, P, NPANEL, 0>(st, alpha, scale != 0, typename traits<T>::real(0));
+    }
 }
 
 // Compute units of the current device (cached per device).
@@ -832,12 +1000,15 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
     const int64_t blocks = (items + 3) / 4;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     // Whole 64-row columns in registers for f32, f64 and c64 (no re-reads of
-    // finished rows); two row panels for c128, whose full column would take
-    // all 256 VGPRs. Measured on MI355X against 2/2/4 panels at 4 waves per
-    // SIMD: f64 139 -> 114 us, c64 149 -> 136 us, c128 422 -> 291 us per
-    // 4096 problems (re-read rows had been evicted from L2 and came back
-    // from HBM).
-    constexpr int NP = sizeof(T) == 16 ? 2 : 1;
+    // finished rows), solved in one panel (f32) or in four one-line panels
+    // (f64, c64: the next panel's B lines load while a panel is solved;
+    // 4096 problems on MI355X: f64 83.6 -> 80.4 us, c64 114 -> 109 us, f32
+    // 38.8 -> 43.8 us, so f32 stays whole); two row panels for c128, whose
+    // full column would take all 256 VGPRs. Measured against re-reading the
+    // finished rows of 2/2/4 panels: f64 139 -> 114 us, c64 149 -> 136 us,
+    // c128 422 -> 291 us per 4096 problems (re-read rows had been evicted
+    // from L2 and came back from HBM).
+    constexpr int NP = kPanels<T>;
     // The 16-byte tile accesses need 16-byte aligned columns.
     if (((uintptr_t)B & 15) != 0 || ((ldb * (int64_t)sizeof(T)) & 15) != 0 ||
         ((strideB * (int64_t)sizeof(T)) & 15) != 0 || ((strideB2 * (int64_t)sizeof(T)) & 15) != 0)
