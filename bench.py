@@ -150,6 +150,49 @@ def bench_batched(hs, torch, steps, warmup, m=64, n=64, batch=4096, check=True):
             "wall_s": wall, "host": host}
 
 
+def bench_batched_alone(hs, torch, host, m=64, n=64, batch=4096, launches=20):
+    """Each dtype's batched launches back to back, with no other dtype in between (in the step,
+    every launch follows another dtype's launch and measures slower). A ring of copies larger than
+    the 256 MB last-level cache keeps every launch reading from HBM; HIP events around the
+    group of launches on the launch stream, mean per launch."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for dt in DTYPES:
+        A, B = host[dt]
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        set_bytes = (dA.numel() + dB.numel()) * dA.element_size()
+        ns = max(2, -(-640 * 2 ** 20 // set_bytes))
+        ring = [(dA.clone(), dB.clone()) for _ in range(ns)]
+        del dA, dB
+        f = hs.entry("strided_batched", dt)
+
+        def launch(i):
+            a, b = ring[i % ns]
+            st = f(m, n, 1.0, a, m, m * m, b, m, m * n, batch, stream)
+            if st != hs.SUCCESS:
+                raise hs.HsmaError(st, "strided_batched_" + dt)
+
+        for i in range(ns):
+            launch(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(launches):
+            launch(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / launches
+        nbytes = small_bytes(dt, m, n) * batch
+        out[dt] = {"ms_per_launch": ms, "gflops": lapack_flops(dt, m, n) * batch / ms / 1e6,
+                   "hbm_gbs": nbytes / ms / 1e6, "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS,
+                   "launches": launches, "ring_copies": ns}
+        del ring
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_solve_tri(hs, torch, runs=2000, n=64, k=6, e2=4, e3=2):
     """A SOLVE_TRI shape of the llama.cpp PR, f32, ggml layout: by default its
     performance shape A [64,64,4,2], B [6,64,4,2]; with n = 128, k = 8, e2 = 4,
@@ -508,8 +551,8 @@ def counter_workload(hs, torch):
 # Valid only for the kernel source they were taken on: keyed by the SHA-256 of
 # small.hip.
 MEASURED_TRAFFIC = {
-    "cda86369dde8bb1a8e5a2a52c77e32e8c3ddc926b6a8152a73a39123fb34717c": {
-        "f32": 185330176, "f64": 353128747, "c64": 357351680, "c128": 852590123},
+    "8d6c08ba7b1e55286cf06bd036e3dd6e187fccd161610d579e13e7b3527799f8": {
+        "f32": 185325440, "f64": 353134123, "c64": 357223467, "c128": 852528341},
 }
 
 
@@ -605,6 +648,8 @@ def main():
     bt = bench_batched(hs, torch, args.steps, args.warmup)
     per = bt["per_dtype"]
     dom = max(per, key=lambda d: per[d]["ms_per_launch"])
+    log("batched launches of one dtype back to back")
+    alone = bench_batched_alone(hs, torch, bt["host"])
     log("solve_tri shape")
     st = bench_solve_tri(hs, torch)
     log("solve_tri 128 shape")
@@ -632,6 +677,7 @@ def main():
                      "kernel": "colane_kernel (%s), %d algorithmic bytes per launch" % (dom, per[dom]["bytes_per_launch"])},
         "cpu_baseline": cpu,
         "per_dtype": per,
+        "per_dtype_alone": alone,
         "solve_tri": st, "solve_tri_128": st128, "solve_tri_256": st256,
         "blocked_8192": blocked,
         "blocked_16384": blocked16,

@@ -112,6 +112,25 @@ def test_throughput_batch_4096(hs, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n", [64, 96])
+def test_launch_size_forms_bitwise_equal(hs, dtype, n):
+    """f64 and c64 solve the problems of a launch with many problems per CU in four row panels
+    and those of a smaller launch in one pass; every element takes its updates in the same
+    order either way, so the same problems must give the same bits in both (the other dtypes
+    have one form and must agree as well). n = 96: a second, ragged group of columns."""
+    say("launch forms", dtype, n)
+    A, B = colmajor_inputs(dtype, 64, n, 4096, seed=0x5EED0007, offdiag_div=64)
+    Xbig = solve_batched(hs, dtype, A, B, 64, n, 64, 64)
+    Xsmall = solve_batched(hs, dtype, np.ascontiguousarray(A[:256]), np.ascontiguousarray(B[:256]),
+                           64, n, 64, 64)
+    assert np.array_equal(Xbig[:256].view(np.uint8), Xsmall.view(np.uint8))
+    sel = np.arange(0, 4096, 16)
+    err = check(dtype, np.ascontiguousarray(A[sel]), np.ascontiguousarray(B[sel]),
+                np.ascontiguousarray(Xbig[sel]), 64, 1.0)
+    say("  rel err", err)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("m,n", [(64, 64), (40, 5)])
 def test_exact_integer_cases_bitwise(hs, dtype, m, n):
     """Bidiagonal (1, -1) gives running sums, all-ones lower gives differences:

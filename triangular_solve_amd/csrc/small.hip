@@ -487,20 +487,21 @@ struct TouchPlan {
     static constexpr Table T = build();
 };
 
-// Kept-column panels (f64, c64): the whole 64-row column stays in registers
-// and is solved in row panels of one 128-byte line; a panel applies the
-// finished rows of the earlier panels straight from registers (no row is read
-// back from memory, and each element sees its updates in the same order as
-// in one panel), while the next panel's lines of B are on their way. f32
-// solves its kept column in one panel; double complex keeps only its current
-// panel (a whole column would take all 256 VGPRs) and reads the earlier rows
-// back from X.
-template <typename T>
-constexpr bool kKeep = sizeof(T) == 8;
+// Kept-column panels (f64, c64 in launches of many problems): the whole
+// 64-row column stays in registers and is solved in row panels of one
+// 128-byte line; a panel applies the finished rows of the earlier panels
+// straight from registers (no row is read back from memory, and each element
+// sees its updates in the same order as in one panel), while the next panel's
+// lines of B are on their way. f32, and f64 and c64 in smaller launches,
+// solve the kept column in one panel (P = 64); double complex keeps only its
+// current panel (a whole column would take all 256 VGPRs) and reads the
+// earlier rows back from X.
+template <typename T, int P>
+constexpr bool kKeep = sizeof(T) == 8 && P < 64;
 
-// Row panels per 64-row column.
+// Rows per kept-column panel (one 128-byte line).
 template <typename T>
-constexpr int kPanels = kKeep<T> ? 64 * (int)sizeof(T) / 128 : sizeof(T) == 16 ? 2 : 1;
+constexpr int kKeepRows = 128 / (int)sizeof(T);
 
 // Where the coefficient prefetch loads land. Their results are never used;
 // a load into registers has to be waited for before the registers are
@@ -509,15 +510,15 @@ constexpr int kPanels = kKeep<T> ? 64 * (int)sizeof(T) / 128 : sizeof(T) == 16 ?
 // direct them into a few LDS bytes that nothing reads.
 // For the single-panel f32 solve the waits are harmless and the LDS form
 // measured slower (38.4 -> 47.5 us per 4096 problems).
-template <typename T>
-constexpr bool kTouchLds = kKeep<T>;
+template <typename T, int P>
+constexpr bool kTouchLds = kKeep<T, P>;
 
 // Registers of a lane's column, and the register of panel row 0 of the panel
 // at rows R0.
 template <typename T, int P>
-constexpr int kRegs = kKeep<T> ? 64 : P;
-template <typename T, int R0>
-constexpr int kRegOff = kKeep<T> ? R0 : 0;
+constexpr int kRegs = kKeep<T, P> ? 64 : P;
+template <typename T, int P, int R0>
+constexpr int kRegOff = kKeep<T, P> ? R0 : 0;
 
 // Per-panel state shared by the batch recursion below.
 template <typename T, int P>
@@ -692,9 +693,9 @@ __device__ __forceinline__ void batch_compute(PanelState<T, P> &st, const T (&cb
         using Plan = PanelPlan<P, R0, G, kDiagInStream<T>>;
         constexpr auto pc = Plan::T.pc[Q];
         constexpr int off = Plan::T.off[Q];
-        constexpr int wo = kRegOff<T, R0>;
+        constexpr int wo = kRegOff<T, P, R0>;
         if constexpr (pc.first) {
-            if constexpr (pc.reload && kKeep<T>) {
+            if constexpr (pc.reload && kKeep<T, P>) {
                 // finished x_k of an earlier panel, still in its register
                 st.x = st.w[pc.col];
             } else if constexpr (pc.reload) {
@@ -759,7 +760,7 @@ __device__ __forceinline__ void batch_touch(PanelState<T, P> &st, cptr<T> ap)
         const int bytes = (int)(first - line) + (sg.hi - sg.lo) * (int)sizeof(T);
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void *)line, (short)0, bytes, 0x00020000);
-        if constexpr (kTouchLds<T>)
+        if constexpr (kTouchLds<T, P>)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)st.sink, 4,
                                                      st.lane128, 0, 0, 0);
         else
@@ -793,7 +794,7 @@ __device__ __forceinline__ void run_batches(PanelState<T, P> &st)
         batch_touch<T, P, R0, G, AH, TP::T.tfirst[Bi], TP::T.tfirst[Bi + 1]>(st, ap);
         T cb[G];
         batch_load<T, P, R0, G, p0, p1>(cb, ap, st.lda);
-        if constexpr (!kTouchLds<T>) batch_retire<T, P, TP::T.cfirst[Bi], TP::T.cfirst[Bi + 1]>(st);
+        if constexpr (!kTouchLds<T, P>) batch_retire<T, P, TP::T.cfirst[Bi], TP::T.cfirst[Bi + 1]>(st);
         batch_compute<T, P, R0, G, p0, p1>(st, cb);
         __builtin_amdgcn_sched_barrier(0);
         run_batches<T, P, R0, G, AH, Bi + 1>(st);
@@ -955,7 +956,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 4 ? 4 : 2) colane_kernel(con
     st.sink = (lptr)colane_sink;
 
     st.lane128 = lane * 128;
-    if constexpr (kKeep<T> && NPANEL > 1) {
+    if constexpr (kKeep<T, P>) {
         const gptr<T> bw = (gptr<T>)(uint64_t)Bc0;
         v4i nb[8];
         panel_issue<T, P>(st, bw, 0, nb);
@@ -1000,15 +1001,20 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
     const int64_t blocks = (items + 3) / 4;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     // Whole 64-row columns in registers for f32, f64 and c64 (no re-reads of
-    // finished rows), solved in one panel (f32) or in four one-line panels
-    // (f64, c64: the next panel's B lines load while a panel is solved;
-    // 4096 problems on MI355X: f64 83.6 -> 80.4 us, c64 114 -> 109 us, f32
-    // 38.8 -> 43.8 us, so f32 stays whole); two row panels for c128, whose
-    // full column would take all 256 VGPRs. Measured against re-reading the
-    // finished rows of 2/2/4 panels: f64 139 -> 114 us, c64 149 -> 136 us,
-    // c128 422 -> 291 us per 4096 problems (re-read rows had been evicted
-    // from L2 and came back from HBM).
-    constexpr int NP = kPanels<T>;
+    // finished rows); two row panels for c128, whose full column would take
+    // all 256 VGPRs. Measured against re-reading the finished rows of 2/2/4
+    // panels: f64 139 -> 114 us, c64 149 -> 136 us, c128 422 -> 291 us per
+    // 4096 problems (re-read rows had been evicted from L2 and came back from
+    // HBM). f64 and c64 solve the kept column in four one-line panels when a
+    // launch has many problems per CU, so the next panel's B lines load while
+    // a panel is solved, and in one panel otherwise; f32 loses with panels
+    // (38.8 -> 43.8 us per 4096 problems). Per launch on MI355X, one panel
+    // against four: f64 1024 problems 31.1 / 32.2 us, 2048: 41.0 / 42.8,
+    // 2560: 63.2 / 61.8, 3072: 71.0 / 67.7, 4096: 85.8 / 82.6; c64 1024:
+    // 44.7 / 46.7, 2048: 60.3 / 62.0, 3072: 91.2 / 93.4, 4096: 111.7 / 108.9.
+    constexpr int NP = sizeof(T) == 16 ? 2 : 1;
+    constexpr int64_t kPanelsFromPerCu = traits<T>::is_complex ? 16 : 10;
+    const bool panels = sizeof(T) == 8 && items >= kPanelsFromPerCu * num_cus();
     // The 16-byte tile accesses need 16-byte aligned columns.
     if (((uintptr_t)B & 15) != 0 || ((ldb * (int64_t)sizeof(T)) & 15) != 0 ||
         ((strideB * (int64_t)sizeof(T)) & 15) != 0 || ((strideB2 * (int64_t)sizeof(T)) & 15) != 0)
@@ -1022,6 +1028,14 @@ hipError_t small_colane2(int64_t n, T alpha, const T *A, int64_t lda, int64_t st
     if (per_cu >= 3 && per_cu < 8) {
         const size_t share = ((size_t)(160 * 1024) / (size_t)per_cu) & ~(size_t)1023;
         if (share > lds) lds = share;
+    }
+    if constexpr (sizeof(T) == 8) {
+        if (panels) {
+            hipLaunchKernelGGL((colane_kernel<T, 64 / kKeepRows<T>>), dim3((unsigned)blocks), dim3(256), lds, s,
+                               A, lda, strideA, B, ldb, strideB, n, nchunks, items, alpha, is_one(alpha) ? 0 : 1,
+                               per, strideA2, strideB2);
+            return hipGetLastError();
+        }
     }
     hipLaunchKernelGGL((colane_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), lds, s, A, lda,
                        strideA, B, ldb, strideB, n, nchunks, items, alpha, is_one(alpha) ? 0 : 1, per, strideA2,
