@@ -225,53 +225,72 @@ hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *in
 // for A, so every k is still summed exactly once).
 
 // NI x NJ blocks of BLK x BLK outputs per wave (NI along the rows i of C, NJ
-// along its columns j), four waves as 2 x 2, so a workgroup tile is
-// BM = 2*NI*BLK rows by BN = 2*NJ*BLK columns; K steps of BK. TILE selects
-// the standard tile, the tall f32 tile for large products or the 64 x 64
-// tile for products with few standard tiles.
-constexpr int kTileStd = 0, kTileWide = 1, kTileSmall = 2;
+// along its columns j), WI x WJ waves, so a workgroup tile is BM = WI*NI*BLK
+// rows by BN = WJ*NJ*BLK columns; K steps of BK. TILE selects the standard
+// tile, the large f32 tiles for large products or the 64 x 64 tile for
+// products with few standard tiles.
+constexpr int kTileStd = 0, kTileWide = 1, kTileSmall = 2, kTileBig = 3;
 template <typename R, int TILE = kTileStd> struct mfma_cfg;
 // FP32: v_mfma_f32_32x32x2f32, a wave owns 64 x 64 outputs as 2 x 2 blocks.
 template <> struct mfma_cfg<float, kTileStd> {
+    static constexpr int WI = 2, WJ = 2;
     static constexpr int BLK = 32, LG = 2, NI = 2, NJ = 2, BK = 32;  // LG: lane groups along k
     using acc_t = f32x16;
     static constexpr int NACC = 16;
-    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
 };
 // FP32, wide: a wave owns 128 x 64 outputs as 4 x 2 blocks, a 256 x 128
 // workgroup tile with K steps of 16: a third fewer LDS bytes per MFMA and
 // more flops per byte of L2 traffic. It wins on large products (the trailing
 // updates, K >= 2048) and loses where its coarser tiles leave CUs idle.
 template <> struct mfma_cfg<float, kTileWide> {
+    static constexpr int WI = 2, WJ = 2;
     static constexpr int BLK = 32, LG = 2, NI = 4, NJ = 2, BK = 16;
     using acc_t = f32x16;
     static constexpr int NACC = 16;
-    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
+};
+// FP32, big: the wide tile's waves, eight of them, as a 256 x 256 workgroup
+// tile (232 VGPRs: one workgroup per CU): half the A and B bytes fetched per
+// output. For real f32 products it replaces the wide tile (MI355X:
+// 6144 x 8192 x 2048 1.93 -> 1.88 ms, 4096 x 8192 x 2048 1.16 -> 1.12 ms,
+// 2048 x 8192 x 2048 0.575 -> 0.56 ms); complex products, whose A is expanded
+// on its way into LDS, lose with it (c64 6144 x 8192 x 2048 6.94 -> 7.14 ms)
+// and keep the wide tile.
+template <> struct mfma_cfg<float, kTileBig> {
+    static constexpr int WI = 2, WJ = 4;
+    static constexpr int BLK = 32, LG = 2, NI = 4, NJ = 2, BK = 16;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
 };
 // FP32, small: a wave owns one 32 x 32 block, a 64 x 64 workgroup tile: four
 // times the workgroups of the standard tile for products that would leave
 // CUs idle (the block-inverse merges, single problems in block rows, the
 // products of mid-size solves).
 template <> struct mfma_cfg<float, kTileSmall> {
+    static constexpr int WI = 2, WJ = 2;
     static constexpr int BLK = 32, LG = 2, NI = 1, NJ = 1, BK = 32;
     using acc_t = f32x16;
     static constexpr int NACC = 16;
-    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
 };
 // FP64: v_mfma_f64_16x16x4f64, a wave owns 64 x 64 outputs as 4 x 4 blocks
 // (a larger tile would double the 128-register accumulator).
 template <> struct mfma_cfg<double, kTileStd> {
+    static constexpr int WI = 2, WJ = 2;
     static constexpr int BLK = 16, LG = 4, NI = 4, NJ = 4, BK = 8;
     using acc_t = f64x4;
     static constexpr int NACC = 4;
-    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
 };
 // FP64, small: a wave owns 32 x 32 outputs as 2 x 2 blocks, a 64 x 64 tile.
 template <> struct mfma_cfg<double, kTileSmall> {
+    static constexpr int WI = 2, WJ = 2;
     static constexpr int BLK = 16, LG = 4, NI = 2, NJ = 2, BK = 8;
     using acc_t = f64x4;
     static constexpr int NACC = 4;
-    static constexpr int BM = 2 * NI * BLK, BN = 2 * NJ * BLK;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
 };
 
 __device__ inline f32x16 mfma_op(float a, float b, f32x16 c)
@@ -316,7 +335,7 @@ struct GemmArgs {
 };
 
 template <typename T, bool VEC, int TILE>
-__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
+__global__ void __launch_bounds__((mfma_cfg<typename traits<T>::real, TILE>::NT), 2) gemm_kernel(GemmArgs<T> p)
 {
     using R = typename traits<T>::real;
     using cfg = mfma_cfg<R, TILE>;
@@ -335,8 +354,8 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wi = (wave & 1) * (NI * BLK);   // wave's row offset inside the tile (i)
-    const int wj = (wave >> 1) * (NJ * BLK);  // wave's column offset (j)
+    const int wi = (wave % cfg::WI) * (NI * BLK);  // wave's row offset inside the tile (i)
+    const int wj = (wave / cfg::WI) * (NJ * BLK);  // wave's column offset (j)
     // Tile of this workgroup. Workgroups are dealt to the 8 XCDs round-robin
     // by linear id, and each XCD has its own L2; for a single product the
     // ids are renumbered so that every XCD gets a contiguous range, walked in
@@ -374,10 +393,11 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
 
     // ---- staging of one K step: A as 16-byte chunks along i, B along k ----
     // A tile: BK x kBM reals = (kBM/VN) chunks per k row; chunks per thread:
-    constexpr int A_CH = BK * kBM / VN / 256;
-    constexpr int B_CH = BK * kBN / VN / 256;
-    static_assert(A_CH * 256 * VN == BK * kBM && B_CH * 256 * VN == BK * kBN,
-                  "the 256 threads' 16-byte chunks cover a K step's tiles exactly");
+    constexpr int NT = cfg::NT;
+    constexpr int A_CH = BK * kBM / VN / NT;
+    constexpr int B_CH = BK * kBN / VN / NT;
+    static_assert(A_CH * NT * VN == BK * kBM && B_CH * NT * VN == BK * kBN,
+                  "the threads' 16-byte chunks cover a K step's tiles exactly");
     // PF K steps of staging registers: step s+PF is fetched while step s is
     // multiplied (with PF = 2, s+1 already sits in the other LDS buffer).
     // Measured on MI355X, PF = 2 gained nothing over PF = 1, which needs
@@ -396,7 +416,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
             if (fast) {
 #pragma unroll
                 for (int e = 0; e < A_CH; ++e) {
-                    const int idx = tid + 256 * e;
+                    const int idx = tid + NT * e;
                     const int ic = idx % (kBM / VN), kl = idx / (kBM / VN);
                     if constexpr (CPX) {
                         // 16 bytes = VN/2 complex entries of complex column (k0+kl)/2;
@@ -415,7 +435,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
                 }
 #pragma unroll
                 for (int e = 0; e < B_CH; ++e) {
-                    const int idx = tid + 256 * e;
+                    const int idx = tid + NT * e;
                     const int kc = idx % (BK / VN), jl = idx / (BK / VN);
                     rb[slot][e] = *(const V16 *)(p.B + k0 + kc * VN + (j0 + jl) * p.ldb);
                 }
@@ -424,7 +444,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
         }
 #pragma unroll
         for (int e = 0; e < A_CH; ++e) {
-            const int idx = tid + 256 * e;
+            const int idx = tid + NT * e;
             const int ic = idx % (kBM / VN), kl = idx / (kBM / VN);  // chunk column, k row
             const int64_t k = k0 + kl;
             V16 v;
@@ -465,7 +485,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
         }
 #pragma unroll
         for (int e = 0; e < B_CH; ++e) {
-            const int idx = tid + 256 * e;
+            const int idx = tid + NT * e;
             const int kc = idx % (BK / VN), jl = idx / (BK / VN);
             const int64_t kb = k0 + kc * VN, j = j0 + jl;
             V16 v;
@@ -481,13 +501,13 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmArgs<T> p)
     auto store_step = [&](int buf, int slot) {
 #pragma unroll
         for (int e = 0; e < A_CH; ++e) {
-            const int idx = tid + 256 * e;
+            const int idx = tid + NT * e;
             const int ic = idx % (kBM / VN), kl = idx / (kBM / VN);
             *(V16 *)&As[buf][kl * LDA_S + ic * VN] = ra[slot][e];
         }
 #pragma unroll
         for (int e = 0; e < B_CH; ++e) {
-            const int idx = tid + 256 * e;
+            const int idx = tid + NT * e;
             const int kc = idx % (BK / VN), jl = idx / (BK / VN);
             *(V16 *)&Bs[buf][jl * LDB_S + kc * VN] = rb[slot][e];
         }
@@ -612,14 +632,16 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
         p.alpha = alpha;
         p.cscale = beta / alpha;
     }
-    // the wide f32 tile for large full products: K of 2048 or more and at
-    // least two wide tiles per CU (a triangular product keeps the finer
-    // tiles, which balance its uneven rows better)
-    using CW = mfma_cfg<R, std::is_same<R, float>::value ? kTileWide : kTileStd>;
+    // the large f32 tiles for large full products: K of 2048 or more and at
+    // least one big tile per CU for real f32 (a 256 x 256 tile, eight waves),
+    // two wide tiles per CU for c64 (256 x 128, four waves); a triangular
+    // product keeps the finer tiles, which balance its uneven rows better
+    constexpr bool kBigF = std::is_same<T, float>::value;
+    using CW = mfma_cfg<R, std::is_same<R, float>::value ? (kBigF ? kTileBig : kTileWide) : kTileStd>;
     using CS = mfma_cfg<R, kTileStd>;
     using CM = mfma_cfg<R, kTileSmall>;
     const bool wide = std::is_same<R, float>::value && !a_lower && p.Kr >= 2048 &&
-                      ((p.Mr + CW::BM - 1) / CW::BM) * ((N + CW::BN - 1) / CW::BN) * batch >= 512;
+                      ((p.Mr + CW::BM - 1) / CW::BM) * ((N + CW::BN - 1) / CW::BN) * batch >= (kBigF ? 256 : 512);
     // the 64 x 64 tile: for fewer than two standard tiles per CU (four times
     // the workgroups of the same product; measured on MI355X against a limit
     // of one per CU, 1.0-1.27x faster solves, and mixed, 0.96-1.16x, at
@@ -641,8 +663,9 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)batch);
     if constexpr (std::is_same<R, float>::value) {
         if (wide) {
-            if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileWide>), grid, dim3(256), 0, s, p);
-            else hipLaunchKernelGGL((gemm_kernel<T, false, kTileWide>), grid, dim3(256), 0, s, p);
+            constexpr int TW = kBigF ? kTileBig : kTileWide;
+            if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, TW>), grid, dim3(CW::NT), 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<T, false, TW>), grid, dim3(CW::NT), 0, s, p);
             return hipGetLastError();
         }
     }
