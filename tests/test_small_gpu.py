@@ -248,10 +248,11 @@ def test_repeat_runs_bitwise_identical(hs, dtype):
     """Race detector: the kernels are deterministic, so any run-to-run
     difference is a race. 1000 runs of each path (small regime in both
     kernels, the 64 < m <= 256 band, the blocked path with split products),
-    each compared with the first bit for bit on the device."""
+    each compared with the first bit for bit on the device. The batch of 4096 runs the row-panel
+    form of f64 and c64."""
     import torch
-    cases = [(64, 64, 16, None), (64, 10, 16, None), (37, 6, 16, None), (150, 64, 8, None),
-             (300, 40, 1, 128), (1024, 16, 1, 256)]
+    cases = [(64, 64, 16, None), (64, 64, 4096, None), (64, 10, 16, None), (37, 6, 16, None),
+             (150, 64, 8, None), (300, 40, 1, 128), (1024, 16, 1, 256)]
     for (m, n, batch, nb) in cases:
         say("repeat x1000", dtype, m, n, batch, nb)
         A, B = colmajor_inputs(dtype, m, n, batch, seed=21)
