@@ -81,6 +81,34 @@ def test_gemm_integer_exact(hs, dtype):
     assert np.array_equal(dC.cpu().numpy().T.astype(ref.dtype), ref)
 
 
+@pytest.mark.parametrize("dtype,real", [("c64", "f32"), ("c128", "f64")])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 1024), (300, 130, 70), (1024, 256, 512)])
+def test_complex_gemm_equals_its_real_form_bitwise(hs, dtype, real, M, N, K):
+    """The blocked solve runs large complex trailing products as real ones on A's panel expanded
+    to 2 x 2 real blocks [[re, -im], [im, re]]. The complex GEMM builds the same blocks on its way
+    into LDS and takes each output's products in the same order, so C -= A B must give the same
+    bits both ways (the real form may run another tile: the order within a wave is the same)."""
+    import torch
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    A = rand(dtype, (K, M), rng)             # column-major: [k, :] is column k
+    B = rand(dtype, (N, K), rng)
+    C = rand(dtype, (N, M), rng)
+    rdt = synth.NP_DTYPE[real]
+    Ar = A.view(rdt)                          # (K, 2M): column k as (re, im) pairs
+    E = np.empty((2 * K, 2 * M), dtype=rdt)   # the real form, column-major 2M x 2K
+    E[0::2] = Ar
+    E[1::2, 0::2] = -Ar[:, 1::2]
+    E[1::2, 1::2] = Ar[:, 0::2]
+    say("complex vs real form", dtype, M, N, K)
+    dA, dB, dC1 = to_dev(A), to_dev(B), to_dev(C)
+    dE, dC2 = to_dev(E), to_dev(C)
+    assert hs.entry("gemm", dtype)(M, N, K, -1.0, dA, M, dB, K, 1.0, dC1, M, 0) == hs.SUCCESS
+    assert hs.entry("gemm", real)(2 * M, N, 2 * K, -1.0, dE, 2 * M, dB.view(torch.float32 if real == "f32" else torch.float64),
+                                  2 * K, 1.0, dC2.view(torch.float32 if real == "f32" else torch.float64), 2 * M, 0) == hs.SUCCESS
+    torch.cuda.synchronize()
+    assert torch.equal(dC1.view(torch.uint8), dC2.view(torch.uint8))
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("m,nb", [(100, 64), (256, 128), (1000, 256), (700, 512), (48, 64)])
 def test_diag_inv(hs, dtype, m, nb):

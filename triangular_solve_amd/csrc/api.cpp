@@ -310,7 +310,7 @@ hsma_status trsm_impl(int64_t m, int64_t n, T alpha, const T *A, int64_t lda, in
         rec.cap = opts->n_events;
     }
 
-    const int64_t welems = blocked_workspace_elems(m, n, nb);
+    const int64_t welems = blocked_workspace_elems<T>(m, n, nb);
     void *work = nullptr;
     if (workspace_alloc(&work, (size_t)welems * sizeof(T), s) != hipSuccess || !work) {
         (void)hipGetLastError();
@@ -463,7 +463,7 @@ hsma_status trsm_variant_impl(int side, int uplo, int trans, int diag, int64_t m
         // (left side, no reversal), then the canonical blocked solve
         const bool b_direct = v.sbi == 1 && v.boff == 0;
         const int nb = choose_nb(dt, M, N);
-        const int64_t wblk = blocked_workspace_elems(M, N, nb);
+        const int64_t wblk = blocked_workspace_elems<T>(M, N, nb);
         const size_t elems = (size_t)(M * M + (b_direct ? 0 : M * N) + wblk);
         if (workspace_alloc(&work, elems * sizeof(T), s) != hipSuccess || !work) {
             (void)hipGetLastError();

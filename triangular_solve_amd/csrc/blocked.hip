@@ -1087,6 +1087,16 @@ __global__ void __launch_bounds__(256) copy_kernel(const T *__restrict__ W, int6
         B[i + col * ldb] = W[i + col * ldw];
 }
 
+// Elements of T for the complex trailing panel in real form, 2 x 2 reals per
+// complex entry: at most (m - nb) x nb entries (0 for real types).
+template <typename T>
+static int64_t expand_elems(int64_t m, int nb)
+{
+    if (!traits<T>::is_complex || m <= nb) return 0;
+    return 2 * (m - nb) * (int64_t)nb;
+}
+
+template <typename T>
 int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
 {
     const int64_t nt = (m + nb - 1) / nb;
@@ -1094,7 +1104,9 @@ int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb)
     const int64_t t = blocked_inverse_temp_elems(m, nb);
     if (t > w) w = t;  // the merge temporaries live in W before W is used
     w = (w + 63) / 64 * 64;   // the split-K partials start 256-byte aligned
-    return nt * nb * nb + w + splitk_part_elems(m, n);
+    const int64_t ex = expand_elems<T>(m, nb);
+    const int64_t part = (splitk_part_elems(m, n) + 63) / 64 * 64;
+    return nt * nb * nb + w + part + ex;
 }
 
 template <typename T>
@@ -1121,10 +1133,35 @@ hipError_t blocked_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T 
     return diag_invert<T>(m, nb, ib, A, lda, invA, s);
 }
 
+// The complex panel P (M x K, column-major, ld lda) in real form E (2M x 2K,
+// column-major, ld 2M): entry (i, k) becomes the 2 x 2 block [[re, -im],
+// [im, re]] at rows 2i, 2i+1 and columns 2k, 2k+1, so E's column 2k is P's
+// column k read as reals and column 2k+1 is (-im, re) pairs. The real
+// product E * W (W read as real, 2K x n) is the complex product P * W with
+// every real multiply-add of the complex kernel, which builds the same
+// blocks on its way into LDS; expanding once per block row instead of per
+// tile fetch halves the loads of A's panel and lets the product run as a
+// real one.
+template <typename R>
+__global__ void __launch_bounds__(256) expand_kernel(const cplx<R> *__restrict__ P, int64_t lda, int64_t M,
+                                                     R *__restrict__ E)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t k = blockIdx.y;
+    if (i >= M) return;
+    const cplx<R> a = P[i + k * lda];
+    R *e0 = E + 2 * k * (2 * M) + 2 * i;
+    R *e1 = e0 + 2 * M;
+    e0[0] = a.re;
+    e0[1] = a.im;
+    e1[0] = -a.im;
+    e1[1] = a.re;
+}
+
 template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
                          T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec, T *part,
-                         int64_t part_elems, const CopyOverlap *ov)
+                         int64_t part_elems, const CopyOverlap *ov, T *expand)
 {
     using R = typename traits<T>::real;
     const int64_t nt = (m + nb - 1) / nb;
@@ -1165,8 +1202,24 @@ hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, 
         // B_t, so it runs beside the copy
         if (e == hipSuccess && r0 + rb < m) {
             e = mark(HSMA_PHASE_TRAILING);
-            if (e == hipSuccess)
-                e = gemm_splitk<T>(m - r0 - rb, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb,
+            const int64_t mt = m - r0 - rb;
+            bool done = false;
+            if constexpr (traits<T>::is_complex) {
+                // complex products that would not be split along K: the panel
+                // in real form once, then the real product
+                const int64_t S = part ? splitk_chunks<T>(mt, n, rb, part_elems) : 1;
+                if (e == hipSuccess && expand && S == 1 && mt <= 0x7fffffffLL * 256 && rb <= 65535) {
+                    hipLaunchKernelGGL(expand_kernel<R>, dim3((unsigned)((mt + 255) / 256), (unsigned)rb),
+                                       dim3(256), 0, s, A + (r0 + rb) + r0 * lda, lda, mt, (R *)expand);
+                    e = hipGetLastError();
+                    if (e == hipSuccess)
+                        e = gemm<R>(2 * mt, n, 2 * rb, R(-1), (const R *)expand, 2 * mt, (const R *)W,
+                                    2 * (int64_t)nb, R(1), (R *)(B + r0 + rb), 2 * ldb, false, s);
+                    done = true;
+                }
+            }
+            if (e == hipSuccess && !done)
+                e = gemm_splitk<T>(mt, n, rb, R(-1), A + (r0 + rb) + r0 * lda, lda, W, nb,
                                    R(1), B + r0 + rb, ldb, false, part, part_elems, s);
         }
         // s does not go on to overwrite W (next block row) or finish before
@@ -1200,6 +1253,8 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     wlen = (wlen + 63) / 64 * 64;
     T *part = W + wlen;           // split-K partial products (few right-hand sides)
     const int64_t part_elems = splitk_part_elems(m, n);
+    // complex: the trailing panel in real form (after the partials, 256-byte aligned)
+    T *expand = expand_elems<T>(m, nb) > 0 ? part + (part_elems + 63) / 64 * 64 : nullptr;
     hipError_t e = rec ? rec->mark(HSMA_PHASE_DIAG_INV, s) : hipSuccess;
     if (e == hipSuccess) e = blocked_invert<T>(m, nb, ib, A, lda, invA, W, s, route);
     if (e != hipSuccess) return e;
@@ -1212,7 +1267,7 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     const bool overlap2 = overlap &&
                           hipEventCreateWithFlags(&ov.copied, hipEventDisableTiming) == hipSuccess;
     e = blocked_apply<T>(m, n, nb, A, lda, invA, B, ldb, W, s, rec, part_elems ? part : nullptr,
-                         part_elems, overlap2 ? &ov : nullptr);
+                         part_elems, overlap2 ? &ov : nullptr, expand);
     // (events still pending are released by the runtime once they complete)
     if (overlap) (void)hipEventDestroy(ov.ready);
     if (overlap2) (void)hipEventDestroy(ov.copied);
@@ -1237,7 +1292,8 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
                                           hipStream_t, int);                                      \
     template hipError_t blocked_apply<T>(int64_t, int64_t, int, const T *, int64_t, const T *, T *, \
                                          int64_t, T *, hipStream_t, PhaseRec *, T *, int64_t,   \
-                                         const CopyOverlap *);
+                                         const CopyOverlap *, T *);                              \
+    template int64_t blocked_workspace_elems<T>(int64_t, int64_t, int);
 HSMA_INST(float)
 HSMA_INST(double)
 HSMA_INST(c32)

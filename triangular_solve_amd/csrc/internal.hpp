@@ -101,8 +101,9 @@ struct PhaseRec {
 inline int blocked_phase_events(int64_t nt) { return (int)(3 * nt + 1); }
 
 // Whole blocked solve of one problem (B already scaled by alpha), with a
-// caller-provided workspace of blocked_workspace_elems(m, n, nb) elements.
+// caller-provided workspace of blocked_workspace_elems<T>(m, n, nb) elements.
 // rec (nullable) records the phase events.
+template <typename T>
 int64_t blocked_workspace_elems(int64_t m, int64_t n, int nb);
 template <typename T>
 hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64_t lda, T *B,
@@ -129,7 +130,7 @@ template <typename T>
 hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, const T *invA,
                          T *B, int64_t ldb, T *W, hipStream_t s, PhaseRec *rec = nullptr,
                          T *part = nullptr, int64_t part_elems = 0,
-                         const CopyOverlap *ov = nullptr);
+                         const CopyOverlap *ov = nullptr, T *expand = nullptr);
 
 // The second stream of the current device for the blocked path's copies
 // (created on first use, default priority, kept until the process ends).
