@@ -491,7 +491,9 @@ def medium_workload(hs, torch, m=128, n=64, batch=1024, reps=5):
 def gemm_workload(hs, torch, shapes=((7168, 8192, 1024), (6144, 8192, 2048)), reps=5):
     """The library GEMM at trailing-update shapes of the blocked solve
     (C -= A B, beta = 1), per dtype, against torch's own matmul on the same
-    shapes for context (not part of any path)."""
+    shapes for context (not part of any path); for the complex types also
+    the real form of the product, which the blocked solve's trailing updates
+    run."""
     out = {}
     stream = torch.cuda.current_stream()
     tdt = {"f32": torch.float32, "f64": torch.float64, "c64": torch.complex64, "c128": torch.complex128}
@@ -520,9 +522,20 @@ def gemm_workload(hs, torch, shapes=((7168, 8192, 1024), (6144, 8192, 2048)), re
             ms_t = timed(lambda: Ct.addmm_(At, Bt, alpha=-1))
             flops = (8 if dt.startswith("c") else 2) * M * N * K
             peak = MFMA_PEAK_TFLOPS[dt]
-            out["%s %dx%dx%d" % (dt, M, N, K)] = {
-                "ms": ms, "tflops": flops / ms / 1e9, "mfma_peak_frac": flops / ms / 1e9 / peak,
-                "torch_ms": ms_t, "torch_mfma_peak_frac": flops / ms_t / 1e9 / peak}
+            row = {"ms": ms, "tflops": flops / ms / 1e9, "mfma_peak_frac": flops / ms / 1e9 / peak,
+                   "torch_ms": ms_t, "torch_mfma_peak_frac": flops / ms_t / 1e9 / peak}
+            if dt.startswith("c"):
+                # the form the blocked solve's trailing updates take: A's panel as 2 x 2
+                # real blocks (2M x 2K), B and C read as real matrices, the real product
+                rdt = "f32" if dt == "c64" else "f64"
+                E = torch.rand(2 * K, 2 * M, device="cuda", generator=g, dtype=tdt[rdt])
+                Br, Cr = torch.view_as_real(Bm), torch.view_as_real(C)
+                fr = hs.entry("gemm", rdt)
+                ms_r = timed(lambda: hs.check(fr(2 * M, N, 2 * K, -1.0, E, 2 * M, Br, 2 * K, 1.0, Cr, 2 * M, 0,
+                                                 stream), "gemm_" + rdt))
+                row.update({"real_form_ms": ms_r, "real_form_mfma_peak_frac": flops / ms_r / 1e9 / peak})
+                del E
+            out["%s %dx%dx%d" % (dt, M, N, K)] = row
             del A, Bm, C
     return out
 
