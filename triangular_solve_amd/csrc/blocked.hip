@@ -229,7 +229,7 @@ hipError_t diag_invert(int64_t m, int nb, int ib, const T *A, int64_t lda, T *in
 // rows by BN = WJ*NJ*BLK columns; K steps of BK. TILE selects the standard
 // tile, the large f32 tiles for large products or the 64 x 64 tile for
 // products with few standard tiles.
-constexpr int kTileStd = 0, kTileWide = 1, kTileSmall = 2, kTileBig = 3;
+constexpr int kTileStd = 0, kTileWide = 1, kTileSmall = 2, kTileBig = 3, kTileStd8 = 4;
 template <typename R, int TILE = kTileStd> struct mfma_cfg;
 // FP32: v_mfma_f32_32x32x2f32, a wave owns 64 x 64 outputs as 2 x 2 blocks.
 template <> struct mfma_cfg<float, kTileStd> {
@@ -260,6 +260,16 @@ template <> struct mfma_cfg<float, kTileWide> {
 template <> struct mfma_cfg<float, kTileBig> {
     static constexpr int WI = 2, WJ = 4;
     static constexpr int BLK = 32, LG = 2, NI = 4, NJ = 2, BK = 16;
+    using acc_t = f32x16;
+    static constexpr int NACC = 16;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
+};
+// FP32, standard tile of eight waves: 128 x 256, each wave 64 x 64 (196
+// VGPRs, one workgroup per CU); for real f32 products between the small and
+// the big tile, the triangular inverse multiplies among them.
+template <> struct mfma_cfg<float, kTileStd8> {
+    static constexpr int WI = 2, WJ = 4;
+    static constexpr int BLK = 32, LG = 2, NI = 2, NJ = 2, BK = 32;
     using acc_t = f32x16;
     static constexpr int NACC = 16;
     static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
@@ -673,6 +683,21 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
         if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileSmall>), grid, dim3(256), 0, s, p);
         else hipLaunchKernelGGL((gemm_kernel<T, false, kTileSmall>), grid, dim3(256), 0, s, p);
         return hipGetLastError();
+    }
+    // real f32 products with at least one 128 x 256 tile per CU take the
+    // eight-wave standard tile (MI355X: f32 m = n = 8192 solve 5.75 ->
+    // 5.50 ms, 4096 x 4096 x 1024 0.374 -> 0.357 ms; from 512 tiles up only:
+    // 5.58 ms); the per-wave order of the products is that of the four-wave
+    // tile
+    if constexpr (std::is_same<T, float>::value) {
+        using C8 = mfma_cfg<R, kTileStd8>;
+        const int64_t gx8 = (p.Mr + C8::BM - 1) / C8::BM, gy8 = (N + C8::BN - 1) / C8::BN;
+        if (gx8 * gy8 * batch >= 256 && gy8 <= 65535) {
+            const dim3 grid8((unsigned)gx8, (unsigned)gy8, (unsigned)batch);
+            if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileStd8>), grid8, dim3(C8::NT), 0, s, p);
+            else hipLaunchKernelGGL((gemm_kernel<T, false, kTileStd8>), grid8, dim3(C8::NT), 0, s, p);
+            return hipGetLastError();
+        }
     }
     if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileStd>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((gemm_kernel<T, false, kTileStd>), grid, dim3(256), 0, s, p);
