@@ -377,9 +377,14 @@ hsma_status hsma_diag_inv_ex_z(int64_t m, const hsma_trsm_opts *opts,
  * C M x N, all column-major, on the matrix cores (the update of the trailing
  * rows and the multiply by an inverted diagonal block in the blocked path).
  * alpha and beta are real, beta must be 0 or 1 (beta == 0: C is not read).
- * a_lower != 0 declares A lower triangular with M == K: the kernel then skips
+ * a_lower == 1 declares A lower triangular with M == K: the kernel then skips
  * the zero tiles above the diagonal and treats those entries as exact zeros
- * (it never reads them). C must not overlap A or B.
+ * (it never reads them). a_lower == 2 (hsma_gemm_s and hsma_gemm_d only, M
+ * even) declares A lower triangular in 2 x 2 blocks, the real form of a
+ * complex lower-triangular matrix (complex entry (i, k) as the block
+ * [[re, -im], [im, re]] at rows 2i, 2i+1 and columns 2k, 2k+1): entries with
+ * k > i | 1 are treated as zeros. Other values of a_lower:
+ * HSMA_STATUS_INVALID_VALUE. C must not overlap A or B.
  */
 hsma_status hsma_gemm_s(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                         const float *B, int64_t ldb, float beta, float *C, int64_t ldc,

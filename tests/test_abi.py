@@ -103,6 +103,12 @@ def test_gemm_and_diag_inv_checks(hs):
     assert g(4, 4, 4, 1, BAD, 4, BAD, 4, 0.5, BAD, 4, 0, 0) == hs.INVALID_VALUE
     assert g(4, 4, 4, 1, BAD, 3, BAD, 4, 0, BAD, 4, 0, 0) == hs.INVALID_SIZE
     assert g(0, 4, 4, 1, None, 1, None, 4, 0, None, 1, 0, 0) == hs.SUCCESS
+    # a_lower: 0, 1 or (real types, M even) 2 = lower triangular in 2 x 2 blocks
+    assert g(4, 4, 4, 1, BAD, 4, BAD, 4, 0, BAD, 4, 3, 0) == hs.INVALID_VALUE
+    assert g(4, 4, 4, 1, BAD, 4, BAD, 4, 0, BAD, 4, -1, 0) == hs.INVALID_VALUE
+    assert g(5, 4, 5, 1, BAD, 5, BAD, 5, 0, BAD, 5, 2, 0) == hs.INVALID_SIZE
+    assert g(0, 4, 0, 1, None, 1, None, 1, 0, None, 1, 2, 0) == hs.SUCCESS
+    assert hs.entry("gemm", "c64")(4, 4, 4, 1, BAD, 4, BAD, 4, 0, BAD, 4, 2, 0) == hs.INVALID_VALUE
     d = hs.entry("diag_inv", "f64")
     assert d(100, 100, 0, BAD, 100, BAD, 0) == hs.INVALID_VALUE
     assert d(100, 128, 1, BAD, 100, BAD, 0) == hs.INVALID_VALUE

@@ -109,6 +109,39 @@ def test_complex_gemm_equals_its_real_form_bitwise(hs, dtype, real, M, N, K):
     assert torch.equal(dC1.view(torch.uint8), dC2.view(torch.uint8))
 
 
+@pytest.mark.parametrize("dtype,real", [("c64", "f32"), ("c128", "f64")])
+@pytest.mark.parametrize("M,N", [(1024, 4096), (300, 130), (2048, 512)])
+def test_complex_lower_gemm_equals_its_real_form_bitwise(hs, dtype, real, M, N):
+    """The inverse multiply with a complex lower-triangular block runs as a real product on the
+    block's real form, which is lower triangular in 2 x 2 blocks (a_lower = 2: entry (i, k) used
+    when k <= i | 1). The upper part holds NaN in both forms and must never be read; the result
+    must match the complex product (a_lower = 1) bit for bit."""
+    import torch
+    rng = np.random.default_rng(M + 5 * N)
+    A = rand(dtype, (M, M), rng)             # column-major: [k, :] is column k
+    L = A.T.copy()
+    L[np.triu_indices(M, 1)] = np.nan
+    A = np.ascontiguousarray(L.T)
+    B = rand(dtype, (N, M), rng)
+    C = rand(dtype, (N, M), rng)
+    rdt = synth.NP_DTYPE[real]
+    Ar = A.view(rdt)
+    E = np.empty((2 * M, 2 * M), dtype=rdt)
+    E[0::2] = Ar
+    E[1::2, 0::2] = -Ar[:, 1::2]
+    E[1::2, 1::2] = Ar[:, 0::2]
+    say("complex lower vs real form", dtype, M, N)
+    dA, dB, dC1 = to_dev(A), to_dev(B), to_dev(C)
+    dE, dC2 = to_dev(E), to_dev(C)
+    tr = torch.float32 if real == "f32" else torch.float64
+    assert hs.entry("gemm", dtype)(M, N, M, 1.0, dA, M, dB, M, 0.0, dC1, M, 1) == hs.SUCCESS
+    assert hs.entry("gemm", real)(2 * M, N, 2 * M, 1.0, dE, 2 * M, dB.view(tr), 2 * M, 0.0, dC2.view(tr),
+                                  2 * M, 2) == hs.SUCCESS
+    torch.cuda.synchronize()
+    assert torch.equal(dC1.view(torch.uint8), dC2.view(torch.uint8))
+    assert not torch.isnan(dC1.view(tr)).any()
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("m,nb", [(100, 64), (256, 128), (1000, 256), (700, 512), (48, 64)])
 def test_diag_inv(hs, dtype, m, nb):

@@ -530,11 +530,13 @@ hsma_status gemm_impl(int64_t M, int64_t N, int64_t K, typename traits<T>::real 
 {
     if (M < 0 || N < 0 || K < 0) return HSMA_STATUS_INVALID_SIZE;
     if (lda < imax(1, M) || ldb < imax(1, K) || ldc < imax(1, M)) return HSMA_STATUS_INVALID_SIZE;
+    if (a_lower < 0 || a_lower > 2 || (a_lower == 2 && traits<T>::is_complex)) return HSMA_STATUS_INVALID_VALUE;
     if (a_lower && M != K) return HSMA_STATUS_INVALID_SIZE;
+    if (a_lower == 2 && M % 2 != 0) return HSMA_STATUS_INVALID_SIZE;
     if (!(beta == 0 || beta == 1)) return HSMA_STATUS_INVALID_VALUE;
     if (M == 0 || N == 0) return HSMA_STATUS_SUCCESS;
     if (!C || (K > 0 && (!A || !B))) return HSMA_STATUS_INVALID_POINTER;
-    return hip_status(gemm<T>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower != 0,
+    return hip_status(gemm<T>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, a_lower,
                               (hipStream_t)stream));
 }
 

@@ -418,10 +418,13 @@ __global__ void __launch_bounds__((mfma_cfg<typename traits<T>::real, TILE>::NT)
     // Interior tiles and steps (the common case) take branch-free 16-byte
     // loads; the bounds and triangle checks only run at the edges.
     int64_t kend = p.Kr;
-    if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal
+    if (p.a_lower && i0 + kBM < kend) kend = i0 + kBM;  // A is zero right of the diagonal (block)
     const bool tile_interior = VEC && i0 + kBM <= p.Mr && j0 + kBN <= p.N;
     auto load_step = [&](int64_t k0, int slot) {
-        const bool fast = tile_interior && k0 + BK <= p.Kr && (!p.a_lower || k0 + BK <= i0 + 1);
+        // a_lower 2 (the real form of a complex lower triangle): entry (i, k)
+        // is used when k <= i | 1, so a step is whole when it ends at i0 + 1
+        const int blk2 = p.a_lower == 2;
+        const bool fast = tile_interior && k0 + BK <= p.Kr && (!p.a_lower || k0 + BK <= i0 + 1 + blk2);
         {
             if (fast) {
 #pragma unroll
@@ -479,14 +482,14 @@ __global__ void __launch_bounds__((mfma_cfg<typename traits<T>::real, TILE>::NT)
                 for (int t = 0; t < VN; ++t) v[t] = tmp[t];
             } else {
                 const int64_t ib = i0 + (int64_t)ic * VN;
-                const bool full = VEC && ib + VN <= p.Mr && k < p.Kr && (!p.a_lower || k <= ib);
+                const bool full = VEC && ib + VN <= p.Mr && k < p.Kr && (!p.a_lower || k <= ib + blk2);
                 if (full) {
                     v = *(const V16 *)(p.A + ib + k * p.lda);
                 } else {
 #pragma unroll
                     for (int t = 0; t < VN; ++t) {
                         const int64_t i = ib + t;
-                        const bool ok = i < p.Mr && k < p.Kr && (!p.a_lower || k <= i);
+                        const bool ok = i < p.Mr && k < p.Kr && (!p.a_lower || k <= (i | blk2));
                         v[t] = ok ? p.A[i + k * p.lda] : R(0);
                     }
                 }
@@ -612,7 +615,7 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
                                const T *A, int64_t lda, int64_t sAi, int64_t sAo, const T *B,
                                int64_t ldb, int64_t sBi, int64_t sBo, typename traits<T>::real beta,
                                T *C, int64_t ldc, int64_t sCi, int64_t sCo, int64_t bin,
-                               int64_t batch, bool a_lower, hipStream_t s)
+                               int64_t batch, int a_lower, hipStream_t s)
 {
     using R = typename traits<T>::real;
     constexpr int f = traits<T>::is_complex ? 2 : 1;
@@ -627,7 +630,7 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
     p.Mr = M * f;
     p.N = N;
     p.Kr = K * f;
-    p.a_lower = a_lower ? 1 : 0;
+    p.a_lower = a_lower;
     p.bin = bin > 0 ? bin : 1;
     p.sAi = sAi; p.sAo = sAo;
     p.sBi = sBi * f; p.sBo = sBo * f;
@@ -724,7 +727,7 @@ hipError_t gemm_strided(int64_t M, int64_t N, int64_t K, typename traits<T>::rea
 template <typename T>
 hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
                 int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
-                int64_t ldc, bool a_lower, hipStream_t s)
+                int64_t ldc, int a_lower, hipStream_t s)
 {
     return gemm_batched<T>(M, N, K, alpha, A, lda, 0, 0, B, ldb, 0, 0, beta, C, ldc, 0, 0, 1, 1,
                            a_lower, s);
@@ -1112,13 +1115,15 @@ __global__ void __launch_bounds__(256) copy_kernel(const T *__restrict__ W, int6
         B[i + col * ldb] = W[i + col * ldw];
 }
 
-// Elements of T for the complex trailing panel in real form, 2 x 2 reals per
-// complex entry: at most (m - nb) x nb entries (0 for real types).
+// Elements of T for a complex trailing panel or inverted diagonal block in
+// real form, 2 x 2 reals per complex entry: at most max(m - nb, nb) x nb
+// entries (0 for real types).
 template <typename T>
 static int64_t expand_elems(int64_t m, int nb)
 {
-    if (!traits<T>::is_complex || m <= nb) return 0;
-    return 2 * (m - nb) * (int64_t)nb;
+    if (!traits<T>::is_complex) return 0;
+    const int64_t rows = m - nb > nb ? m - nb : nb;  // a trailing panel or a diagonal block
+    return 2 * rows * (int64_t)nb;
 }
 
 template <typename T>
@@ -1197,7 +1202,22 @@ hipError_t blocked_apply(int64_t m, int64_t n, int nb, const T *A, int64_t lda, 
         const int64_t rb = m - r0 < nb ? m - r0 : nb;
         // X_t = D_t^{-1} B_t (D_t^{-1} is lower triangular: upper tiles skipped)
         e = mark(HSMA_PHASE_INV_GEMM);
-        if (e == hipSuccess)
+        bool inv_done = false;
+        if constexpr (traits<T>::is_complex) {
+            // products that would not be split along K: the inverted block in
+            // real form (lower triangular in 2 x 2 blocks), then the real product
+            const int64_t S = part ? splitk_chunks<T>(rb, n, rb, part_elems) : 1;
+            if (e == hipSuccess && expand && S == 1) {
+                hipLaunchKernelGGL(expand_kernel<R>, dim3((unsigned)((rb + 255) / 256), (unsigned)rb), dim3(256), 0,
+                                   s, invA + t * nb * nb, (int64_t)nb, rb, (R *)expand);
+                e = hipGetLastError();
+                if (e == hipSuccess)
+                    e = gemm<R>(2 * rb, n, 2 * rb, R(1), (const R *)expand, 2 * rb, (const R *)(B + r0),
+                                2 * ldb, R(0), (R *)W, 2 * (int64_t)nb, 2, s);
+                inv_done = true;
+            }
+        }
+        if (e == hipSuccess && !inv_done)
             e = gemm_splitk<T>(rb, n, rb, R(1), invA + t * nb * nb, nb, B + r0, ldb, R(0), W, nb, true,
                                part, part_elems, s);
         if (e == hipSuccess) e = mark(HSMA_PHASE_COPY);
@@ -1306,7 +1326,7 @@ hipError_t blocked_solve(int64_t m, int64_t n, int nb, int ib, const T *A, int64
     template bool invert_route_applies<T>(int64_t, int, int, int);                                \
     template hipError_t gemm<T>(int64_t, int64_t, int64_t, typename traits<T>::real, const T *,    \
                                 int64_t, const T *, int64_t, typename traits<T>::real, T *,       \
-                                int64_t, bool, hipStream_t);                                      \
+                                int64_t, int, hipStream_t);                                       \
     template hipError_t gemm_strided<T>(int64_t, int64_t, int64_t, typename traits<T>::real,       \
                                         const T *, int64_t, int64_t, const T *, int64_t, int64_t, \
                                         typename traits<T>::real, T *, int64_t, int64_t, int64_t, \

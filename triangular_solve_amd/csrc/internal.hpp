@@ -66,12 +66,14 @@ hipError_t diag_invert_any(int64_t m, int nb, int ib, const T *A, int64_t lda, T
 template <typename T>
 bool invert_route_applies(int64_t m, int nb, int ib, int route);
 
-// C = beta*C + alpha*A*B on the matrix cores (beta in {0, 1}); a_lower: A is
-// lower triangular (M == K) and its upper tiles are skipped.
+// C = beta*C + alpha*A*B on the matrix cores (beta in {0, 1}); a_lower 1: A
+// is lower triangular (M == K) and its upper tiles are skipped; 2 (real
+// types): A is lower triangular in 2 x 2 blocks, the real form of a complex
+// lower-triangular matrix (entry (i, k) is used when k <= i | 1).
 template <typename T>
 hipError_t gemm(int64_t M, int64_t N, int64_t K, typename traits<T>::real alpha, const T *A,
                 int64_t lda, const T *B, int64_t ldb, typename traits<T>::real beta, T *C,
-                int64_t ldc, bool a_lower, hipStream_t s);
+                int64_t ldc, int a_lower, hipStream_t s);
 
 // Strided-batched C_z = beta*C_z + alpha*A_z*B_z, z < batch (A_z = A + z*strideA,
 // alike for B and C; strideA may be 0).
