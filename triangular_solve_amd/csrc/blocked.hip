@@ -294,6 +294,16 @@ template <> struct mfma_cfg<double, kTileStd> {
     static constexpr int NACC = 4;
     static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
 };
+// FP64, standard tile of eight waves: 128 x 256, each wave 64 x 64, for
+// the triangular products of real f64 (the inverse multiplies of f64 and,
+// in real form, of c128).
+template <> struct mfma_cfg<double, kTileStd8> {
+    static constexpr int WI = 2, WJ = 4;
+    static constexpr int BLK = 16, LG = 4, NI = 4, NJ = 4, BK = 8;
+    using acc_t = f64x4;
+    static constexpr int NACC = 4;
+    static constexpr int BM = WI * NI * BLK, BN = WJ * NJ * BLK, NT = 64 * WI * WJ;
+};
 // FP64, small: a wave owns 32 x 32 outputs as 2 x 2 blocks, a 64 x 64 tile.
 template <> struct mfma_cfg<double, kTileSmall> {
     static constexpr int WI = 2, WJ = 2;
@@ -687,15 +697,16 @@ static hipError_t gemm_batched(int64_t M, int64_t N, int64_t K, typename traits<
         else hipLaunchKernelGGL((gemm_kernel<T, false, kTileSmall>), grid, dim3(256), 0, s, p);
         return hipGetLastError();
     }
-    // real f32 products with at least one 128 x 256 tile per CU take the
-    // eight-wave standard tile (MI355X: f32 m = n = 8192 solve 5.75 ->
-    // 5.50 ms, 4096 x 4096 x 1024 0.374 -> 0.357 ms; from 512 tiles up only:
-    // 5.58 ms); the per-wave order of the products is that of the four-wave
-    // tile
-    if constexpr (std::is_same<T, float>::value) {
+    // real f32 products, and triangular real f64 ones, with at least one
+    // 128 x 256 tile per CU take the eight-wave standard tile (MI355X: f32
+    // m = n = 8192 solve 5.75 -> 5.50 ms, 4096 x 4096 x 1024 0.374 -> 0.357
+    // ms, from 512 tiles up only 5.58 ms; f64 m = n = 8192 10.22 -> 10.08 ms,
+    // c128 37.97 -> 37.62 ms; full f64 products lose with it); the per-wave
+    // order of the products is that of the four-wave tile
+    if constexpr (std::is_same<T, float>::value || std::is_same<T, double>::value) {
         using C8 = mfma_cfg<R, kTileStd8>;
         const int64_t gx8 = (p.Mr + C8::BM - 1) / C8::BM, gy8 = (N + C8::BN - 1) / C8::BN;
-        if (gx8 * gy8 * batch >= 256 && gy8 <= 65535) {
+        if ((std::is_same<T, float>::value || a_lower) && gx8 * gy8 * batch >= 256 && gy8 <= 65535) {
             const dim3 grid8((unsigned)gx8, (unsigned)gy8, (unsigned)batch);
             if (vec) hipLaunchKernelGGL((gemm_kernel<T, true, kTileStd8>), grid8, dim3(C8::NT), 0, s, p);
             else hipLaunchKernelGGL((gemm_kernel<T, false, kTileStd8>), grid8, dim3(C8::NT), 0, s, p);
